@@ -1,0 +1,125 @@
+/*
+ * flint_moe.h - C ABI of the MI355X (gfx950) library for the Flint per-token
+ * mixture-of-experts FFN block.
+ *
+ * The block (How to Run Flint Locally, "The architecture, from config.json",
+ * table rows "Hidden size", "Routed experts", "Shared expert", and the
+ * paragraph on the MoE block after the table; TandemLLM "21 Flint", 21.1 table
+ * row "MLP"):
+ *   a   = bf16(rmsnorm(x))                               block input (W4A16)
+ *   s   = sigmoid(Wr a),  c = s + b                      router, bias for selection
+ *   T   = the 6 experts with the largest c (ties: lower index)
+ *   w_i = s_i / sum_{j in T} s_j                          normalised top-k weights
+ *   y_e = Wd_e (silu(Wg_e a) * (Wu_e a))                  SwiGLU experts, size 512
+ *   out = x + sum_{i in T} w_i y_i + y_shared             shared expert, size 1024
+ * applied layer after layer over the 47 MoE layers (same section, table row
+ * "Layers"), with the residual kept in fp32 between layers.  Every token is
+ * independent: its result does not depend on the other tokens of the call
+ * (Flint preview, "What is in it": batched requests give the same output as
+ * running alone).
+ *
+ * Weight format (the library's own int4 layout; the pages publish weights in
+ * formats not present here): symmetric two's-complement int4 codes in [-8, 7],
+ * two per byte along the input dimension K (byte j of a row holds k = 2j in
+ * bits 0-3 and k = 2j + 1 in bits 4-7), and one bf16 scale per (row, group of
+ * FLINT_GROUP consecutive k): W[r][k] = code[r][k] * scale[r][k / FLINT_GROUP].
+ * Weights are read as given and copied losslessly into library-owned memory at
+ * create time (vLLM recipe "Flint", guide "Overview": the NVFP4 checkpoint is
+ * repacked losslessly at load and run weight-only with bf16 activations).
+ *
+ * Errors: every call returns FLINT_OK (0) or a negative status; the text of the
+ * last failure on the calling thread is flint_moe_last_error().  Arguments are
+ * validated before anything is enqueued.  Faults inside kernels surface at the
+ * caller's stream synchronisation; flint_moe_status() reports the library's own
+ * device-side checks.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed Flint dimensions (config table of the pages). */
+#define FLINT_HIDDEN       2048  /* H */
+#define FLINT_EXPERTS      256   /* E, routed experts per layer */
+#define FLINT_EXPERT_SIZE  512   /* I */
+#define FLINT_SHARED_SIZE  1024  /* I_s */
+#define FLINT_TOP_K        6
+#define FLINT_GROUP        128   /* K-group of one bf16 scale */
+#define FLINT_MAX_LAYERS   64
+#define FLINT_MAX_TOKENS   2048
+
+#define FLINT_OK                 0
+#define FLINT_ERR_INVALID_ARG   -1  /* null pointer, bad count, range or alignment */
+#define FLINT_ERR_OUT_OF_MEMORY -2  /* device allocation failed */
+#define FLINT_ERR_HIP           -3  /* HIP runtime or launch error */
+#define FLINT_ERR_UNSUPPORTED   -4  /* request outside what this build supports */
+#define FLINT_ERR_DEVICE        -5  /* a device-side check fired (see last_error) */
+
+typedef struct flint_moe* flint_moe_t;
+
+/* One int4 matrix: codes [rows][K/2] bytes and scales [rows][K/FLINT_GROUP]
+ * bf16 bit patterns, both row-major, device pointers.  For per-expert
+ * matrices the experts are stored one after another (expert-major). */
+typedef struct {
+  const uint8_t* codes;
+  const uint16_t* scales;
+} flint_q4;
+
+/* One MoE layer, all device pointers (16-byte aligned).
+ *   router_w    [E][H]   bf16 bits
+ *   router_bias [E]      fp32
+ *   gate, up    [E][I][H/2] codes,  [E][I][H/G] scales
+ *   down        [E][H][I/2] codes,  [E][H][I/G] scales
+ *   sh_gate, sh_up  [I_s][H/2] codes, [I_s][H/G] scales
+ *   sh_down     [H][I_s/2] codes,   [H][I_s/G] scales                       */
+typedef struct {
+  const uint16_t* router_w;
+  const float* router_bias;
+  flint_q4 gate, up, down;
+  flint_q4 sh_gate, sh_up, sh_down;
+} flint_moe_layer;
+
+/* Create a handle holding n_layers layers (1 <= n_layers <= FLINT_MAX_LAYERS)
+ * on the current HIP device.  Synchronous: the weights are copied into memory
+ * the library owns, so the caller may free its buffers when the call returns.
+ * `weights` is a host array of n_layers descriptors of device pointers.
+ * On failure *out is set to NULL and nothing is leaked. */
+int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* out);
+
+/* Apply layers [layer_begin, layer_end) to n_tokens independent fp32 residual
+ * rows x [n_tokens][H] (device), writing out [n_tokens][H] (device).  out == x
+ * is allowed; partial overlap is not.  1 <= n_tokens <= FLINT_MAX_TOKENS and
+ * 0 <= layer_begin < layer_end <= n_layers.  Asynchronous on `stream` (a
+ * hipStream_t; NULL = the default stream).  One handle serves one stream at a
+ * time: calls on a handle must not overlap.  For n_tokens <= 16 each token's
+ * result is bitwise independent of n_tokens; larger calls take the prefill
+ * path (grouped MFMA GEMM), whose rounding differs (bf16 intermediates). */
+int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_begin,
+                      int layer_end, float* out, void* stream);
+
+/* Record each layer's selection: ids [n_layers][capacity][FLINT_TOP_K] int32
+ * and weights [n_layers][capacity][FLINT_TOP_K] fp32 (device buffers, ordered
+ * by decreasing selection score), written by forward for the layers it runs.
+ * NULL ids disables tracing.  While tracing, forward rejects n_tokens above
+ * `capacity`. */
+int flint_moe_set_trace(flint_moe_t h, int32_t* ids, float* weights, int capacity);
+
+/* Blocking: wait for the handle's work on `stream` and report FLINT_ERR_DEVICE
+ * if a device-side check fired (for example a bounded wait that expired). */
+int flint_moe_status(flint_moe_t h, void* stream);
+
+/* Release the handle and its device memory.  NULL is ignored. */
+void flint_moe_destroy(flint_moe_t h);
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* flint_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLINT_MOE_H */

@@ -1,0 +1,242 @@
+// C ABI of the Flint MoE library: handle, argument validation, the
+// library-owned weight arena, workspaces, tracing and error reporting.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "decode.h"
+#include "prefill.h"
+
+using namespace flint;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(FLINT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+// byte sizes of one layer's tensors, in arena order
+struct LayerSizes {
+  size_t router = (size_t)E * H * 2, bias = (size_t)E * 4;
+  size_t gate = (size_t)E * I * (H / 2), gate_s = (size_t)E * I * (H / G) * 2;
+  size_t down = (size_t)E * H * (I / 2), down_s = (size_t)E * H * (I / G) * 2;
+  size_t sh_gu = (size_t)IS * (H / 2), sh_gu_s = (size_t)IS * (H / G) * 2;
+  size_t sh_down = (size_t)H * (IS / 2), sh_down_s = (size_t)H * (IS / G) * 2;
+  size_t list[14] = {router, bias, gate, gate_s, gate, gate_s, down, down_s,
+                     sh_gu, sh_gu_s, sh_gu, sh_gu_s, sh_down, sh_down_s};
+  size_t total() const {
+    size_t t = 0;
+    for (size_t s : list) t += align_up(s);
+    return t;
+  }
+};
+
+}  // namespace
+
+struct flint_moe {
+  int device = -1;
+  int n_layers = 0;
+  char* arena = nullptr;
+  std::vector<LayerW> layers;
+  DecodeWS dws{};
+  char* dws_mem = nullptr;
+  PrefillWS pws{};
+  char* pws_mem = nullptr;
+  int* dev_error = nullptr;  // device-side check word
+  int32_t* trace_ids = nullptr;
+  float* trace_w = nullptr;
+  int trace_capacity = 0;
+};
+
+static void release(flint_moe* h) {
+  if (!h) return;
+  if (h->device >= 0) (void)hipSetDevice(h->device);
+  if (h->arena) (void)hipFree(h->arena);
+  if (h->dws_mem) (void)hipFree(h->dws_mem);
+  if (h->pws_mem) (void)hipFree(h->pws_mem);
+  if (h->dev_error) (void)hipFree(h->dev_error);
+  delete h;
+}
+
+static int checked_malloc(void** p, size_t bytes, const char* what) {
+  const char* inj = getenv("FLINT_MOE_FAIL_ALLOC");
+  if (inj && inj[0] == '1') {
+    *p = nullptr;
+    return fail(FLINT_ERR_OUT_OF_MEMORY, "allocation of %zu bytes for %s failed (injected)", bytes, what);
+  }
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+      return fail(FLINT_ERR_OUT_OF_MEMORY, "allocation of %zu bytes for %s failed", bytes, what);
+    return fail_hip(e, "hipMalloc");
+  }
+  return FLINT_OK;
+}
+
+extern "C" {
+
+const char* flint_moe_last_error(void) { return g_last_error.c_str(); }
+
+int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* out) {
+  if (!out) return fail(FLINT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!weights) return fail(FLINT_ERR_INVALID_ARG, "weights is NULL");
+  if (n_layers < 1 || n_layers > FLINT_MAX_LAYERS)
+    return fail(FLINT_ERR_INVALID_ARG, "n_layers = %d outside [1, %d]", n_layers, FLINT_MAX_LAYERS);
+  for (int l = 0; l < n_layers; ++l) {
+    const flint_moe_layer& w = weights[l];
+    const void* ptrs[14] = {w.router_w, w.router_bias, w.gate.codes, w.gate.scales, w.up.codes, w.up.scales,
+                            w.down.codes, w.down.scales, w.sh_gate.codes, w.sh_gate.scales, w.sh_up.codes,
+                            w.sh_up.scales, w.sh_down.codes, w.sh_down.scales};
+    for (int i = 0; i < 14; ++i)
+      if (!ptrs[i]) return fail(FLINT_ERR_INVALID_ARG, "layer %d: tensor %d is NULL", l, i);
+  }
+  flint_moe* h = new flint_moe();
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { int r = fail_hip(e, "hipGetDevice"); h->device = -1; release(h); return r; }
+  h->n_layers = n_layers;
+  LayerSizes sz;
+  const size_t per_layer = sz.total();
+  int rc = checked_malloc((void**)&h->arena, per_layer * n_layers, "weights");
+  if (rc) { release(h); return rc; }
+  h->layers.resize(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    const flint_moe_layer& w = weights[l];
+    const void* src[14] = {w.router_w, w.router_bias, w.gate.codes, w.gate.scales, w.up.codes, w.up.scales,
+                           w.down.codes, w.down.scales, w.sh_gate.codes, w.sh_gate.scales, w.sh_up.codes,
+                           w.sh_up.scales, w.sh_down.codes, w.sh_down.scales};
+    char* base = h->arena + per_layer * l;
+    char* dst[14];
+    size_t off = 0;
+    for (int i = 0; i < 14; ++i) {
+      dst[i] = base + off;
+      e = hipMemcpy(dst[i], src[i], sz.list[i], hipMemcpyDefault);
+      if (e != hipSuccess) { rc = fail_hip(e, "copying weights"); release(h); return rc; }
+      off += align_up(sz.list[i]);
+    }
+    LayerW& L = h->layers[l];
+    L.router = (const uint16_t*)dst[0];
+    L.bias = (const float*)dst[1];
+    L.gate = (const uint8_t*)dst[2];
+    L.gate_s = (const uint16_t*)dst[3];
+    L.up = (const uint8_t*)dst[4];
+    L.up_s = (const uint16_t*)dst[5];
+    L.down = (const uint8_t*)dst[6];
+    L.down_s = (const uint16_t*)dst[7];
+    L.sh_gate = (const uint8_t*)dst[8];
+    L.sh_gate_s = (const uint16_t*)dst[9];
+    L.sh_up = (const uint8_t*)dst[10];
+    L.sh_up_s = (const uint16_t*)dst[11];
+    L.sh_down = (const uint8_t*)dst[12];
+    L.sh_down_s = (const uint16_t*)dst[13];
+  }
+  // decode workspace
+  {
+    const int T = DECODE_MAX_TOKENS;
+    size_t sizes[7] = {(size_t)T * H * 2, (size_t)T * 64 * 4, (size_t)T * E * 8, (size_t)T * TOPK * 4,
+                       (size_t)T * TOPK * 4, (size_t)T * TOPK * I * 4, (size_t)T * IS * 4};
+    size_t tot = 0;
+    for (size_t s : sizes) tot += align_up(s);
+    rc = checked_malloc((void**)&h->dws_mem, tot, "decode workspace");
+    if (rc) { release(h); return rc; }
+    char* p = h->dws_mem;
+    void** dst[7] = {(void**)&h->dws.a, (void**)&h->dws.asum, (void**)&h->dws.z, (void**)&h->dws.ids,
+                     (void**)&h->dws.w, (void**)&h->dws.h, (void**)&h->dws.hsh};
+    for (int i = 0; i < 7; ++i) { *dst[i] = p; p += align_up(sizes[i]); }
+  }
+  rc = prefill_workspace_alloc(&h->pws, &h->pws_mem, checked_malloc);
+  if (rc) { release(h); return rc; }
+  rc = checked_malloc((void**)&h->dev_error, 256, "error word");
+  if (rc) { release(h); return rc; }
+  e = hipMemset(h->dev_error, 0, 256);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) { rc = fail_hip(e, "create"); release(h); return rc; }
+  *out = h;
+  return FLINT_OK;
+}
+
+int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_begin, int layer_end, float* out,
+                      void* stream) {
+  if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+  if (!x || !out) return fail(FLINT_ERR_INVALID_ARG, "x or out is NULL");
+  if (((uintptr_t)x | (uintptr_t)out) & 15) return fail(FLINT_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
+  if (n_tokens < 1 || n_tokens > FLINT_MAX_TOKENS)
+    return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_MAX_TOKENS);
+  if (layer_begin < 0 || layer_end > h->n_layers || layer_begin >= layer_end)
+    return fail(FLINT_ERR_INVALID_ARG, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
+                h->n_layers);
+  const size_t bytes = (size_t)n_tokens * H * sizeof(float);
+  const char *xb = (const char*)x, *ob = (const char*)out;
+  if (xb != ob && xb < ob + bytes && ob < xb + bytes)
+    return fail(FLINT_ERR_INVALID_ARG, "x and out overlap partially");
+  if (h->trace_ids && n_tokens > h->trace_capacity)
+    return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d above the trace capacity %d", n_tokens, h->trace_capacity);
+  hipError_t e = hipSetDevice(h->device);
+  if (e != hipSuccess) return fail_hip(e, "hipSetDevice");
+  hipStream_t s = (hipStream_t)stream;
+  for (int l = layer_begin; l < layer_end; ++l) {
+    const float* xin = (l == layer_begin) ? x : out;
+    int32_t* tid = h->trace_ids ? h->trace_ids + (size_t)l * h->trace_capacity * TOPK : nullptr;
+    float* tw = h->trace_w ? h->trace_w + (size_t)l * h->trace_capacity * TOPK : nullptr;
+    if (n_tokens <= DECODE_MAX_TOKENS)
+      e = launch_decode_layer(xin, out, n_tokens, h->layers[l], h->dws, tid, tw, s);
+    else
+      e = launch_prefill_layer(xin, out, n_tokens, h->layers[l], h->pws, tid, tw, s);
+    if (e == hipErrorNotSupported)
+      return fail(FLINT_ERR_UNSUPPORTED, "n_tokens = %d needs the prefill path, which this build lacks", n_tokens);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  }
+  return FLINT_OK;
+}
+
+int flint_moe_set_trace(flint_moe_t h, int32_t* ids, float* weights, int capacity) {
+  if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+  if (!ids) {
+    h->trace_ids = nullptr;
+    h->trace_w = nullptr;
+    h->trace_capacity = 0;
+    return FLINT_OK;
+  }
+  if (!weights) return fail(FLINT_ERR_INVALID_ARG, "trace weights buffer is NULL");
+  if (capacity < 1 || capacity > FLINT_MAX_TOKENS)
+    return fail(FLINT_ERR_INVALID_ARG, "trace capacity %d outside [1, %d]", capacity, FLINT_MAX_TOKENS);
+  h->trace_ids = ids;
+  h->trace_w = weights;
+  h->trace_capacity = capacity;
+  return FLINT_OK;
+}
+
+int flint_moe_status(flint_moe_t h, void* stream) {
+  if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+  hipError_t e = hipSetDevice(h->device);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  int word = 0;
+  if (e == hipSuccess) e = hipMemcpy(&word, h->dev_error, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(e, "status");
+  if (word) return fail(FLINT_ERR_DEVICE, "device-side check fired (code %d)", word);
+  return FLINT_OK;
+}
+
+void flint_moe_destroy(flint_moe_t h) { release(h); }
+
+}  // extern "C"
