@@ -1,0 +1,197 @@
+"""Benchmark of the Flint MoE block decode on one MI355X.
+
+Workload: the full 47-layer stack at batch 1 (hidden 2048, 256 experts of 512,
+top-6, shared expert 1024, int4 group 128, distinct seeded weights per layer,
+the last ten layers with routed up-projection scales x 4096).  One step = one
+token through all 47 layers (one forward call): RMSNorm, router, top-6,
+gate/up + SwiGLU, down + combine, residual, per layer.  Tokens come from a pool
+of 64 distinct seeded vectors already resident in HBM.
+
+Prints one JSON line.  Use --gpus 1 (this build runs on one GPU).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-block decode tokens/s and achieved HBM GB/s (47-layer int4, batch 1)"
+N_LAYERS = 47
+H, E, I, IS, K, G = 2048, 256, 512, 1024, 6, 128
+PEAK_HBM_GBPS = 8000.0
+
+
+def q4_bytes(rows, k):
+    return rows * k // 2 + rows * (k // G) * 2
+
+
+# Algorithmic bytes one token reads in one layer (what the hot path must read
+# from HBM at least once): bf16 router + fp32 bias, and for each of the six
+# routed experts plus the shared expert their int4 codes and bf16 scales.
+EXPERT_BYTES = 2 * q4_bytes(I, H) + q4_bytes(H, I)            # 1,622,016
+SHARED_BYTES = 2 * q4_bytes(IS, H) + q4_bytes(H, IS)          # 3,244,032
+ROUTER_BYTES = E * H * 2 + E * 4                               # 1,049,600
+LAYER_BYTES = ROUTER_BYTES + K * EXPERT_BYTES + SHARED_BYTES   # 14,025,728
+TOKEN_BYTES = N_LAYERS * LAYER_BYTES                           # 659,209,216
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int4_expert_ffn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_stack47_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds_budget=20.0):
+    """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
+    many of the 47 layers as fit the budget; scaled to tokens/s for the whole
+    stack."""
+    import flintgen as fg
+    from oracle import flint_oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_sources import SynthSource
+    synth = fg.flint_stack(0, N_LAYERS)
+    src = SynthSource(synth)
+    x = fg.token(0, 0)
+    t0 = time.perf_counter()
+    layers = 0
+    for l in range(N_LAYERS):
+        a = O.block_input(x, fg.FLINT)
+        res = O.moe_block(a, src, l, fg.FLINT)
+        x = (x.astype(np.float64) + res.delta).astype(np.float32)
+        layers += 1
+        if time.perf_counter() - t0 > seconds_budget:
+            break
+    dt = time.perf_counter() - t0
+    per_token = dt / layers * N_LAYERS
+    try:
+        import threadpoolctl
+        cores = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    return {"value": round(1.0 / per_token, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 token through layers 0..{layers - 1} of the 47-layer stack ({dt:.1f} s, "
+                      f"weights regenerated per layer included), scaled to 47 layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the per-GPU shard is the whole block, see the sharding note of the design", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 4}))
+        return
+
+    t_setup = time.perf_counter()
+    synth = fg.flint_stack(0, N_LAYERS)
+    layers = []
+    for l in range(N_LAYERS):
+        layers.append(synth.layer(l, dev))
+    torch.cuda.synchronize()
+    model = F.FlintMoE(layers)
+    del layers
+    torch.cuda.empty_cache()
+    pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
+    out = torch.empty((1, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    setup_s = time.perf_counter() - t_setup
+
+    def step(i):
+        F.flint_moe_forward(model.h, pool[i % 64:i % 64 + 1], 1, 0, N_LAYERS, out, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    model.status()
+    # per-launch durations with events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    model.status()
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3   # seconds
+    ms_per_step = wall / args.steps * 1e3
+    value = args.steps / wall
+    launch_s = float(np.mean(durs))
+    achieved = TOKEN_BYTES / launch_s / 1e9
+    traffic = traffic_from_profiles()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xbf16->fp32",
+        "data": "synthetic (seeded int4 weights, bf16 scales, N(0,1) tokens)",
+        "config": {"workload": "47-layer Flint MoE block stack, batch 1 decode", "layers": N_LAYERS,
+                   "hidden": H, "experts": E, "top_k": K, "expert_size": I, "shared_size": IS,
+                   "group": G, "tokens_per_step": 1, "token_pool": 64,
+                   "algorithmic_bytes_per_token": TOKEN_BYTES},
+        "hbm_gbps": round(TOKEN_BYTES * value / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel": "one forward launch sequence (47 layers, 1 token)",
+                     "launch_us_mean": round(launch_s * 1e6, 2),
+                     "launch_us_p10": round(float(np.percentile(durs, 10)) * 1e6, 2),
+                     "launch_us_p90": round(float(np.percentile(durs, 90)) * 1e6, 2)},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,8 @@ struct LayerW {
 struct DecodeWS {
   uint16_t* a;     // [T][H] block input, bf16, pair order
   float* asum;     // [T][64] sums of a over each lane chunk of 32 elements
-  double* z;       // [T][E] router logits
+  double* c;       // [T][E] selection scores sigmoid(z) + b
+  double* s;       // [T][E] sigmoid(z)
   int* ids;        // [T][TOPK]
   float* w;        // [T][TOPK]
   float* h;        // [T][TOPK][I]

@@ -13,7 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/flint_moe.h"
+#include "flint_moe.h"
 
 namespace flint {
 
@@ -53,20 +53,87 @@ __device__ __forceinline__ int perm_order(int k) {
 }
 
 // ------------------------------------------------------------------ reductions
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;  // identical in every lane (each step adds the same two values)
+// Cross-lane moves use DPP (data-parallel primitives: operand routing inside
+// the VALU, a few cycles) rather than LDS permutes.  Controls (GFX9 family):
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7-i within 8
+constexpr int DPP_MIRROR = 0x140;       // lane i <- lane 15-i within 16
+constexpr int DPP_BCAST15 = 0x142;      // row r <- lane 15 of row r-1
+constexpr int DPP_BCAST31 = 0x143;      // rows 2,3 <- lane 31
+
+// Value of `v` moved by a DPP control; lanes outside row_mask receive 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)b), hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// sum over aligned groups of `width` lanes (width a power of two <= 64)
-template <int width, typename T>
-__device__ __forceinline__ T group_sum(T v) {
-#pragma unroll
-  for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+__device__ __forceinline__ float lane_bcast(float v, int lane) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), lane));
+}
+__device__ __forceinline__ double lane_bcast(double v, int lane) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum over each row of 16 lanes; every lane of the row gets the row's sum.
+template <typename T>
+__device__ __forceinline__ T row16_sum(T v) {
+  if constexpr (sizeof(T) == 8) {
+    v += dpp_f64<DPP_XOR1>(v);
+    v += dpp_f64<DPP_XOR2>(v);
+    v += dpp_f64<DPP_HALF_MIRROR>(v);
+    v += dpp_f64<DPP_MIRROR>(v);
+  } else {
+    v += dpp_f32<DPP_XOR1>(v);
+    v += dpp_f32<DPP_XOR2>(v);
+    v += dpp_f32<DPP_HALF_MIRROR>(v);
+    v += dpp_f32<DPP_MIRROR>(v);
+  }
   return v;
 }
+
+// Sum over the wavefront with a fixed tree (rows of 16, then rows 0+1 and
+// 2+3, then all); the total is taken from lane 63 and is the same in every lane.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v = row16_sum(v);
+  if constexpr (sizeof(T) == 8) {
+    v += dpp_f64<DPP_BCAST15, 0xA>(v);
+    v += dpp_f64<DPP_BCAST31, 0xC>(v);
+  } else {
+    v += dpp_f32<DPP_BCAST15, 0xA>(v);
+    v += dpp_f32<DPP_BCAST31, 0xC>(v);
+  }
+  return lane_bcast(v, 63);
+}
+
+// Maximum of a 32-bit unsigned key over the wavefront (same in every lane).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_XOR1>(v));
+  v = max(v, dpp_u32<DPP_XOR2>(v));
+  v = max(v, dpp_u32<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_BCAST15, 0xA>(v));
+  v = max(v, dpp_u32<DPP_BCAST31, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Keep the compiler from moving memory operations across this point (used to
+// issue prefetch loads before a wait loop).  Emits no instruction.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // ------------------------------------------------------------------ int4 dots
 // One code dword holds 8 nibbles (k0..k7).  After xor 0x88888888 each nibble

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "decode.h"
+#include "decode_persistent.h"
 #include "prefill.h"
 
 using namespace flint;
@@ -64,6 +65,14 @@ struct flint_moe {
   int32_t* trace_ids = nullptr;
   float* trace_w = nullptr;
   int trace_capacity = 0;
+  // persistent decode
+  bool persistent = false;
+  LayerW* layers_dev = nullptr;
+  size_t layer_stride = 0;
+  uint64_t* xz = nullptr;
+  uint64_t* xh = nullptr;
+  uint64_t* xx = nullptr;
+  uint32_t epoch = 0;
 };
 
 static void release(flint_moe* h) {
@@ -73,6 +82,10 @@ static void release(flint_moe* h) {
   if (h->dws_mem) (void)hipFree(h->dws_mem);
   if (h->pws_mem) (void)hipFree(h->pws_mem);
   if (h->dev_error) (void)hipFree(h->dev_error);
+  if (h->layers_dev) (void)hipFree(h->layers_dev);
+  if (h->xz) (void)hipFree(h->xz);
+  if (h->xh) (void)hipFree(h->xh);
+  if (h->xx) (void)hipFree(h->xx);
   delete h;
 }
 
@@ -120,6 +133,7 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
   int rc = checked_malloc((void**)&h->arena, per_layer * n_layers, "weights");
   if (rc) { release(h); return rc; }
   h->layers.resize(n_layers);
+  h->layer_stride = per_layer;
   for (int l = 0; l < n_layers; ++l) {
     const flint_moe_layer& w = weights[l];
     const void* src[14] = {w.router_w, w.router_bias, w.gate.codes, w.gate.scales, w.up.codes, w.up.scales,
@@ -153,22 +167,41 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
   // decode workspace
   {
     const int T = DECODE_MAX_TOKENS;
-    size_t sizes[7] = {(size_t)T * H * 2, (size_t)T * 64 * 4, (size_t)T * E * 8, (size_t)T * TOPK * 4,
-                       (size_t)T * TOPK * 4, (size_t)T * TOPK * I * 4, (size_t)T * IS * 4};
+    size_t sizes[8] = {(size_t)T * H * 2, (size_t)T * 64 * 4, (size_t)T * E * 8, (size_t)T * E * 8,
+                       (size_t)T * TOPK * 4, (size_t)T * TOPK * 4, (size_t)T * TOPK * I * 4, (size_t)T * IS * 4};
     size_t tot = 0;
     for (size_t s : sizes) tot += align_up(s);
     rc = checked_malloc((void**)&h->dws_mem, tot, "decode workspace");
     if (rc) { release(h); return rc; }
     char* p = h->dws_mem;
-    void** dst[7] = {(void**)&h->dws.a, (void**)&h->dws.asum, (void**)&h->dws.z, (void**)&h->dws.ids,
-                     (void**)&h->dws.w, (void**)&h->dws.h, (void**)&h->dws.hsh};
-    for (int i = 0; i < 7; ++i) { *dst[i] = p; p += align_up(sizes[i]); }
+    void** dst[8] = {(void**)&h->dws.a, (void**)&h->dws.asum, (void**)&h->dws.c, (void**)&h->dws.s,
+                     (void**)&h->dws.ids, (void**)&h->dws.w, (void**)&h->dws.h, (void**)&h->dws.hsh};
+    for (int i = 0; i < 8; ++i) { *dst[i] = p; p += align_up(sizes[i]); }
   }
   rc = prefill_workspace_alloc(&h->pws, &h->pws_mem, checked_malloc);
   if (rc) { release(h); return rc; }
   rc = checked_malloc((void**)&h->dev_error, 256, "error word");
   if (rc) { release(h); return rc; }
   e = hipMemset(h->dev_error, 0, 256);
+  if (e != hipSuccess) { rc = fail_hip(e, "create"); release(h); return rc; }
+  // persistent decode: needs cooperative launch on exactly NWG compute units
+  {
+    int cus = 0, coop = 0;
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device);
+    const char* mode = getenv("FLINT_MOE_DECODE");
+    const bool layered = mode && strcmp(mode, "layered") == 0;
+    h->persistent = !layered && cus == NWG && coop;
+    rc = checked_malloc((void**)&h->layers_dev, sizeof(LayerW) * n_layers, "layer table");
+    if (!rc) rc = checked_malloc((void**)&h->xz, XZ_WORDS * 8, "exchange z");
+    if (!rc) rc = checked_malloc((void**)&h->xh, XH_WORDS * 8, "exchange h");
+    if (!rc) rc = checked_malloc((void**)&h->xx, XX_WORDS * 8, "exchange x");
+    if (rc) { release(h); return rc; }
+    e = hipMemcpy(h->layers_dev, h->layers.data(), sizeof(LayerW) * n_layers, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(h->xz, 0, XZ_WORDS * 8);
+    if (e == hipSuccess) e = hipMemset(h->xh, 0, XH_WORDS * 8);
+    if (e == hipSuccess) e = hipMemset(h->xx, 0, XX_WORDS * 8);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) { rc = fail_hip(e, "create"); release(h); return rc; }
   *out = h;
@@ -194,6 +227,35 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
   hipError_t e = hipSetDevice(h->device);
   if (e != hipSuccess) return fail_hip(e, "hipSetDevice");
   hipStream_t s = (hipStream_t)stream;
+  if (n_tokens <= DECODE_MAX_TOKENS && h->persistent) {
+    h->epoch += 256;
+    if (h->epoch == 0 || h->epoch > 0xFFFFFE00u) {   // tags wrapped: start again from clean buffers
+      e = clear_exchange(h->xz, XZ_WORDS, s);
+      if (e == hipSuccess) e = clear_exchange(h->xh, XH_WORDS, s);
+      if (e == hipSuccess) e = clear_exchange(h->xx, XX_WORDS, s);
+      if (e != hipSuccess) return fail_hip(e, "clearing exchange buffers");
+      h->epoch = 256;
+    }
+    PersistArgs a;
+    a.x = x;
+    a.out = out;
+    a.n = n_tokens;
+    a.l0 = layer_begin;
+    a.l1 = layer_end;
+    a.base = h->layers[0];
+    a.layer_stride = h->layer_stride;
+    a.xz = h->xz;
+    a.xh = h->xh;
+    a.xx = h->xx;
+    a.trace_ids = h->trace_ids;
+    a.trace_w = h->trace_w;
+    a.trace_cap = h->trace_capacity;
+    a.err = h->dev_error;
+    a.epoch = h->epoch;
+    e = launch_decode_persistent(a, s);
+    if (e != hipSuccess) return fail_hip(e, "persistent decode launch");
+    return FLINT_OK;
+  }
   for (int l = layer_begin; l < layer_end; ++l) {
     const float* xin = (l == layer_begin) ? x : out;
     int32_t* tid = h->trace_ids ? h->trace_ids + (size_t)l * h->trace_capacity * TOPK : nullptr;

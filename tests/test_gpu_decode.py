@@ -162,3 +162,27 @@ def test_allocation_failure_is_reported(model):
         assert ei.value.code == F.FLINT_ERR_OUT_OF_MEMORY
     finally:
         del os.environ["FLINT_MOE_FAIL_ALLOC"]
+
+
+def test_persistent_and_layered_modes_agree_bitwise(model):
+    """The persistent kernel (one launch per call, tagged exchanges between
+    workgroups) and the per-layer kernels run the same arithmetic."""
+    synth, m, ids, w = model
+    layers = build_layers(synth, range(N_LAYERS))
+    os.environ["FLINT_MOE_DECODE"] = "layered"
+    try:
+        m2 = F.FlintMoE(layers)
+    finally:
+        del os.environ["FLINT_MOE_DECODE"]
+    del layers
+    x = torch.from_numpy(fg.tokens(0, range(400, 416))).cuda()
+    try:
+        for n in (1, 4, 9, 16):
+            a = m.forward(x[:n])
+            b = m2.forward(x[:n])
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), n
+        m.status()
+        m2.status()
+    finally:
+        m2.close()
