@@ -7,73 +7,84 @@
 namespace flint {
 
 // ----------------------------------------------------------------- block input
-// Block input of one token into LDS and its 64 lane-chunk sums.
-// 256 threads: thread i owns elements [8 i, 8 i + 8), one pair-order uint4.
-// Layout: the 8-element chunk c = 4 L + j (lane chunk L, j < 4) sits at uint4
-// position j * 64 + L, so lane L reading its four chunks touches consecutive
-// 16-byte slots across lanes (no LDS bank conflicts).
-// RMSNorm in fp64 (squares of fp32 values are exact), one rounding to bf16.
-__device__ __forceinline__ void block_input_to_lds(const float* __restrict__ x, uint4* a_lds, float* asum_lds,
-                                                   double* red) {
-  const int tid = threadIdx.x;
-  const float4* xp = reinterpret_cast<const float4*>(x) + 2 * tid;
-  const float4 v0 = xp[0], v1 = xp[1];
-  const double xs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+constexpr int NT = 512;          // threads per workgroup of the decode kernels
+constexpr int NWAVES = NT / 64;
+
+// Block input of one token: thread i holds elements [4 i, 4 i + 4) of the fp32
+// residual.  RMSNorm in fp64 (squares of fp32 values are exact; per-thread
+// sums, then a fixed wave tree, then the 8 waves in order), one rounding to
+// bf16.  `red` holds NWAVES doubles and must not be reused by the next call
+// before a barrier (callers alternate two buffers).  Writes the activation to LDS in pair order and transposed layout:
+// the 8-element chunk c = 4 L + j (lane chunk L, j < 4) is the uint4 at
+// position j * 64 + L, holding (k0,k2),(k4,k6),(k1,k3),(k5,k7); lane L reading
+// its four chunks touches consecutive 16-byte slots (no bank conflicts).
+// asum_lds[L] = sum of the 32 bf16 values of lane chunk L.
+__device__ __forceinline__ void block_input(float4 xv, uint32_t* a_u32, float* asum_lds, double* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const double xs[4] = {xv.x, xv.y, xv.z, xv.w};
   double ss = 0.0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ss += xs[j] * xs[j];
+  for (int j = 0; j < 4; ++j) ss += xs[j] * xs[j];
   ss = wave_sum(ss);
-  const int wave = tid >> 6, lane = tid & 63;
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  const double tot = ((red[0] + red[1]) + red[2]) + red[3];
-  __syncthreads();
-  const double den = sqrt(tot / (double)H + RMS_EPS);
-  uint32_t b[8];
+  double tot = red[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) tot += red[i];
+  const double ms = tot / (double)H + RMS_EPS;
+  const double rinv = rsqrt(ms);
+  uint32_t b[4];
   float part = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    b[j] = f64_to_bf16_rne(xs[j] / den);
+  for (int j = 0; j < 4; ++j) {
+    // x * rsqrt(ms) is within a few fp64 ulps of x / sqrt(ms); where that
+    // could change the bf16 rounding, use the correctly rounded quotient
+    double q = xs[j] * rinv;
+    if (near_bf16_midpoint(q)) q = xs[j] / sqrt(ms);
+    b[j] = f64_to_bf16_rne(q);
     part += bf16_bits_to_f32(b[j]);
   }
-  // pair order (0,2),(4,6),(1,3),(5,7)
-  a_lds[(tid & 3) * 64 + (tid >> 2)] =
-      make_uint4(b[0] | (b[2] << 16), b[4] | (b[6] << 16), b[1] | (b[3] << 16), b[5] | (b[7] << 16));
-  part += dpp_f32<DPP_XOR1>(part);     // 4 threads = 32 elements = one lane chunk
+  const int c = tid >> 1, half = tid & 1;
+  const int P = ((c & 3) * 64 + (c >> 2)) * 4;
+  a_u32[P + half] = b[0] | (b[2] << 16);       // (k0,k2) or (k4,k6)
+  a_u32[P + 2 + half] = b[1] | (b[3] << 16);   // (k1,k3) or (k5,k7)
+  part += dpp_f32<DPP_XOR1>(part);             // 8 threads = 32 elements = one lane chunk
   part += dpp_f32<DPP_XOR2>(part);
-  if ((tid & 3) == 0) asum_lds[tid >> 2] = part;
+  part += dpp_f32<DPP_HALF_MIRROR>(part);
+  if ((tid & 7) == 0) asum_lds[tid >> 3] = part;
 }
 
-// ----------------------------------------------------------------- router
-// fp64 dot of 8 router weights (natural order) with 8 activations (pair order)
-__device__ __forceinline__ double router_dot8(uint4 w, uint4 a) {
-  // natural k0..k7 from w; activations: a.x=(k0,k2) a.y=(k4,k6) a.z=(k1,k3) a.w=(k5,k7)
-  const float wk[8] = {bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
-                       bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16),
-                       bf16_bits_to_f32(w.z & 0xFFFF), bf16_bits_to_f32(w.z >> 16),
-                       bf16_bits_to_f32(w.w & 0xFFFF), bf16_bits_to_f32(w.w >> 16)};
-  const float ak[8] = {bf16_bits_to_f32(a.x & 0xFFFF), bf16_bits_to_f32(a.z & 0xFFFF),
-                       bf16_bits_to_f32(a.x >> 16), bf16_bits_to_f32(a.z >> 16),
-                       bf16_bits_to_f32(a.y & 0xFFFF), bf16_bits_to_f32(a.w & 0xFFFF),
-                       bf16_bits_to_f32(a.y >> 16), bf16_bits_to_f32(a.w >> 16)};
+// The router row of expert e is split over the 8 waves of a workgroup: lane L
+// of wave v holds the row's 4 weights (8 bytes) for elements 4 (v >> 2) ..
+// 4 (v >> 2) + 3 of 8-element chunk 4 L + (v & 3).
+__device__ __forceinline__ uint2 load_router_part(const uint16_t* router_row) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return reinterpret_cast<const uint2*>(router_row)[2 * (4 * lane + (wave & 3)) + (wave >> 2)];
+}
+
+// This wave's part of the router logit (fp64, same value in every lane).
+__device__ __forceinline__ double router_part(uint2 w, const uint4* a_tok) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint4 a = a_tok[(wave & 3) * 64 + lane];
+  // weights in natural order k0..k3 of the half; activations in pair order
+  const uint32_t alo = (wave >> 2) ? a.y : a.x;   // (k0,k2) or (k4,k6)
+  const uint32_t ahi = (wave >> 2) ? a.w : a.z;   // (k1,k3) or (k5,k7)
+  const float wk[4] = {bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
+                       bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16)};
+  const float ak[4] = {bf16_bits_to_f32(alo & 0xFFFF), bf16_bits_to_f32(ahi & 0xFFFF),
+                       bf16_bits_to_f32(alo >> 16), bf16_bits_to_f32(ahi >> 16)};
   double s = 0.0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s += (double)(wk[j] * ak[j]);   // bf16 x bf16 is exact in fp32
-  return s;
+  for (int j = 0; j < 4; ++j) s += (double)(wk[j] * ak[j]);   // bf16 x bf16 is exact in fp32
+  return wave_sum(s);
 }
 
-// Part of the router logit of one expert row held by wave v: lane L holds the
-// row's weights for chunk 4 L + v (one uint4); summed over the wavefront.
-// The four waves' parts are added in order 0..3 by router_scores().
-__device__ __forceinline__ double router_part(uint4 wr, const uint4* a_tok) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return wave_sum(router_dot8(wr, a_tok[wave * 64 + lane]));
-}
-
-// s = sigmoid(z), c = s + b from the four parts (fp64).  A NaN selection
-// score is replaced by -inf so it never wins.
-__device__ __forceinline__ void router_scores(const double* part4, float bias, double& s, double& c) {
-  const double z = ((part4[0] + part4[1]) + part4[2]) + part4[3];
+// s = sigmoid(z), c = s + b from the 8 wave parts (summed in order, fp64).
+// A NaN selection score is replaced by -inf so it never wins.
+__device__ __forceinline__ void router_scores(const double* part, float bias, double& s, double& c) {
+  double z = part[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) z += part[i];
   s = sigmoid_f64(z);
   c = s + (double)bias;
   if (c != c) c = -INFINITY;
@@ -81,14 +92,14 @@ __device__ __forceinline__ void router_scores(const double* part4, float bias, d
 
 // ----------------------------------------------------------------- selection
 // Order-preserving 32-bit key of a selection score with the expert index in
-// its low byte: the score rounded toward -inf to fp32, mapped so unsigned
-// order equals numeric order, with the low 8 bits replaced by 255 - e (ties
-// in the kept 24 bits go to the lower index).  key(c1) > key(c2) implies
-// c1 > c2 whenever the kept 24 bits differ.
+// its low byte: the top 24 bits of the score's fp64 pattern mapped so that
+// unsigned order equals numeric order (sign, exponent, 12 mantissa bits),
+// with 255 - e below them (ties in the kept bits go to the lower index).
+// key(c1) > key(c2) implies c1 > c2 whenever the kept 24 bits differ.
 __device__ __forceinline__ uint32_t coarse_key(double c, int e) {
-  const uint32_t u = __float_as_uint(__double2float_rd(c));
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (ord & 0xFFFFFF00u) | (uint32_t)(255 - e);
+  const unsigned long long u = (unsigned long long)__double_as_longlong(c);
+  const unsigned long long ord = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return ((uint32_t)(ord >> 32) & 0xFFFFFF00u) | (uint32_t)(255 - e);
 }
 
 // Exact top-k by (c descending, index ascending) with fp64 comparisons;
@@ -145,17 +156,24 @@ __device__ __forceinline__ void route_token(const double* __restrict__ c, const 
   }
   int ids[TOPK];
   if ((picked[TOPK - 1] >> 8) != (picked[TOPK] >> 8)) {
-    // the k-th and (k+1)-th keys differ in their kept bits: the set is exact;
-    // order it by the exact scores (insertion sort, uniform across lanes)
+    // the k-th and (k+1)-th keys differ in their kept bits: the set is exact.
+    // The keys order it exactly too, except inside runs of equal kept bits,
+    // which are re-ordered by the exact scores (rare).
+    bool tie = false;
 #pragma unroll
-    for (int r = 0; r < TOPK; ++r) ids[r] = 255 - (int)(picked[r] & 0xFFu);
+    for (int r = 0; r < TOPK; ++r) {
+      ids[r] = 255 - (int)(picked[r] & 0xFFu);
+      if (r > 0) tie |= (picked[r - 1] >> 8) == (picked[r] >> 8);
+    }
+    if (tie) {
 #pragma unroll
-    for (int i = 1; i < TOPK; ++i) {
+      for (int i = 1; i < TOPK; ++i) {
 #pragma unroll
-      for (int j = i; j > 0; --j) {
-        const int a = ids[j - 1], b = ids[j];
-        const bool swap = c[b] > c[a] || (c[b] == c[a] && b < a);
-        if (swap) { ids[j - 1] = b; ids[j] = a; }
+        for (int j = i; j > 0; --j) {
+          const int a = ids[j - 1], b = ids[j];
+          const bool swap = c[b] > c[a] || (c[b] == c[a] && b < a);
+          if (swap) { ids[j - 1] = b; ids[j] = a; }
+        }
       }
     }
   } else {
@@ -253,13 +271,22 @@ __device__ __forceinline__ void load_down_row(const LayerW& L, const int* ids, i
 
 // One output row of one token by one wavefront: the six routed down rows and
 // the shared one, then out = x + ((((w0 y0 + w1 y1) + w2 y2) + ...) + w5 y5)
-// + y_shared.  ha: this lane's h chunk for pass A (slot lane / 16); hb: for
-// pass B (slot 4 + lane / 16 on lanes 0..31, the shared expert on 32..63).
+// + y_shared.  load_a() gives this lane's h chunk for pass A (slot lane / 16),
+// load_b() for pass B (slot 4 + lane / 16 on lanes 0..31, the shared expert
+// on 32..63); they are called one after the other so only one chunk is live.
 // The result is the same in every lane.
-__device__ __forceinline__ float down_row_token(uint4 ca, float sa, uint4 cb, float sb, const HChunk& ha,
-                                                const HChunk& hb, const float* w, float xres) {
-  const float ya = row16_sum(lane_dot_down(ca, ha.v, ha.sum, sa));
-  const float yb = row16_sum(lane_dot_down(cb, hb.v, hb.sum, sb));
+template <typename LoadA, typename LoadB>
+__device__ __forceinline__ float down_row_token(uint4 ca, float sa, uint4 cb, float sb, LoadA load_a, LoadB load_b,
+                                                const float* w, float xres) {
+  float ya, yb;
+  {
+    const HChunk ha = load_a();
+    ya = row16_sum(lane_dot_down(ca, ha.v, ha.sum, sa));
+  }
+  {
+    const HChunk hb = load_b();
+    yb = row16_sum(lane_dot_down(cb, hb.v, hb.sum, sb));
+  }
   const float ysh = lane_bcast(yb + dpp_f32<DPP_BCAST15, 0x8>(yb), 63);   // rows 2 + 3: shared row
   const float y0 = lane_bcast(ya, 0), y1 = lane_bcast(ya, 16), y2 = lane_bcast(ya, 32), y3 = lane_bcast(ya, 48);
   const float y4 = lane_bcast(yb, 0), y5 = lane_bcast(yb, 16);
@@ -273,24 +300,35 @@ __device__ __forceinline__ float down_row_token(uint4 ca, float sa, uint4 cb, fl
   return xres + d;
 }
 
-// Distinct experts among the picks flagged in mark[E] (non-zero = picked), in
-// increasing id order: on return mark[e] = rank or -1, list[rank] = e.
-// Needs blockDim.x == E; wave_tot is LDS scratch of 4 ints.
-__device__ __forceinline__ int distinct_experts(int* mark, int* list, int* wave_tot) {
+// Distinct experts among the picks ids[0..n)[0..TOPK), in increasing id order,
+// into list[]; returns their number.  Threads 0..E-1 test one expert each.
+__device__ __forceinline__ int distinct_experts(const int (*ids)[TOPK], int n, int* list, int* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int f = mark[tid] != 0;
-  const unsigned long long b = __ballot(f);
-  const int pre = __popcll(b & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[wave] = __popcll(b);
+  int f = 0;
+  if (tid < E)
+    for (int i = 0; i < n * TOPK; ++i) f |= (ids[i / TOPK][i % TOPK] == tid);
+  const unsigned long long bal = __ballot(f);
+  if (lane == 0 && wave < E / 64) wave_tot[wave] = __popcll(bal);
   __syncthreads();
-  int off = 0;
-  for (int i = 0; i < wave; ++i) off += wave_tot[i];
-  const int D = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-  const int r = f ? off + pre : -1;
-  mark[tid] = r;
-  if (f) list[r] = tid;
+  if (f) {
+    int off = __popcll(bal & ((1ull << lane) - 1ull));
+    for (int i = 0; i < wave; ++i) off += wave_tot[i];
+    list[off] = tid;
+  }
+  int D = 0;
+#pragma unroll
+  for (int i = 0; i < E / 64; ++i) D += wave_tot[i];
   __syncthreads();
   return D;
+}
+
+// Slot of expert e in a token's picks, or -1.
+__device__ __forceinline__ int slot_of(const int* ids, int e) {
+  int s = -1;
+#pragma unroll
+  for (int i = TOPK - 1; i >= 0; --i)
+    if (ids[i] == e) s = i;
+  return s;
 }
 
 }  // namespace flint

@@ -2,13 +2,14 @@
 // forward call on 256 workgroups (one per CU), with no kernel boundaries
 // between the dependent stages of a layer.
 //
-// Work of workgroup w (4 wavefronts) in layer l, for each token:
+// Work of workgroup w (8 wavefronts) in layer l, for each token:
 //   P0  block input a = bf16(rmsnorm(x_l)) (every workgroup, redundantly)
-//   P1  router row w -> z[w]; shared-expert gate/up row 4 w + wave -> h_sh
-//   P2  all 256 z -> sigmoid + bias + top-6 (every workgroup, redundantly);
-//       gate/up rows of the distinct picked experts, spread over all waves -> h
-//   P3  all h -> output rows 8 w .. 8 w + 7 (six routed down rows + shared
-//       down row, fixed-order combine) -> x_{l+1}
+//   P1  router row w over all waves -> (c, s) published first; then shared-
+//       expert gate/up row 4 w + wave on waves 0..3 -> h_shared
+//   P2  all 256 (c, s) -> top-6 (every workgroup, redundantly); gate/up rows
+//       of the distinct picked experts, spread over all waves -> h
+//   P3  all h -> output row 8 w + wave (six routed down rows + shared down
+//       row, fixed-order combine) -> x_{l+1}
 // Values cross workgroups through exchange buffers of 64-bit words that carry
 // a 32-bit payload and a 32-bit tag (call epoch, layer, stage).  Writers use
 // relaxed agent-scope atomic stores, readers relaxed agent-scope atomic loads
@@ -25,20 +26,30 @@
 namespace flint {
 
 constexpr int HW = TOPK * I + IS;                  // h words per token (routed, then shared)
+constexpr long long SPIN_TICKS = 100000000LL;      // 1 s of the 100 MHz wall clock
 
 // Phase timestamps for profiling builds only (-DFLINT_PHASE_TS): thread 0 of
-// each workgroup records the 100 MHz wall clock at marker k of layer l.
+// each workgroup records the 100 MHz wall clock at marker k of layer l into
+// LDS (a global store would delay that wave's next poll: its memory counter
+// retires in order), and copies them out when the kernel ends.
 #ifdef FLINT_PHASE_TS
-__device__ unsigned long long g_phase_ts[64][16][NWG];
+constexpr int TS_LAYERS = 48;
+__device__ unsigned long long g_phase_ts[TS_LAYERS][16][NWG];
+__device__ unsigned long long g_gather_ts[TS_LAYERS][4][4];
 #define PHASE_MARK(k) \
-  do { if (threadIdx.x == 0) g_phase_ts[l][k][blockIdx.x] = wall_clock64(); } while (0)
+  do { if (threadIdx.x == 0 && l < TS_LAYERS) ts_lds[l][k] = wall_clock64(); } while (0)
+#define GATHER_PROBE(slot, v) \
+  do { if (threadIdx.x == 0 && dbg_id >= 0 && dbg_layer < TS_LAYERS) gts_lds[dbg_layer][dbg_id][slot] = (v); } while (0)
 extern "C" int flint_moe_debug_phase_ts(unsigned long long* host) {
   return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_ts), sizeof(g_phase_ts));
 }
+extern "C" int flint_moe_debug_gather_ts(unsigned long long* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_gather_ts), sizeof(g_gather_ts));
+}
 #else
 #define PHASE_MARK(k) do { } while (0)
+#define GATHER_PROBE(slot, v) do { } while (0)
 #endif
-constexpr long long SPIN_TICKS = 100000000LL;      // 1 s of the 100 MHz wall clock
 
 __device__ __forceinline__ void publish(uint64_t* p, uint32_t tag, uint32_t v) {
   __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -49,16 +60,22 @@ __device__ __forceinline__ uint64_t load_word(const uint64_t* p) {
 }
 
 // Wait until words src[0..nwords) carry `tag`; store the payload of word j
-// in dst[pos(j)].  Thread i handles words i + 256 k, k < K.  Returns false on
+// in dst[pos(j)].  Thread i handles words i + NT k, k < K.  Returns false on
 // timeout (the device error word is then set).
-template <int K, typename Pos>
+#ifdef FLINT_PHASE_TS
+typedef unsigned long long (*GtsLds)[4][4];
+#else
+typedef void* GtsLds;
+#endif
+template <int K, typename Pos, int NTHR = NT>
 __device__ __forceinline__ bool gather(const uint64_t* src, int nwords, uint32_t tag, uint32_t* dst, int* err,
-                                       Pos pos) {
-  const int tid = threadIdx.x;
+                                       Pos pos, int tid, int dbg_layer, int dbg_id, GtsLds gts_lds) {
+  GATHER_PROBE(0, wall_clock64());
+  unsigned long long iters = 0;
   uint64_t v[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int j = tid + 256 * k;
+    const int j = tid + NTHR * k;
     v[k] = (j < nwords) ? load_word(src + j) : ((uint64_t)tag << 32);
   }
   const long long t0 = wall_clock64();
@@ -68,18 +85,21 @@ __device__ __forceinline__ bool gather(const uint64_t* src, int nwords, uint32_t
     for (int k = 0; k < K; ++k) {
       if ((uint32_t)(v[k] >> 32) != tag) {
         all = false;
-        v[k] = load_word(src + tid + 256 * k);
+        v[k] = load_word(src + tid + NTHR * k);
       }
     }
+    if (iters++ == 0) GATHER_PROBE(1, wall_clock64());
     if (all) break;
     if (wall_clock64() - t0 > SPIN_TICKS) {
       __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
   }
+  GATHER_PROBE(2, wall_clock64());
+  GATHER_PROBE(3, iters);
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int j = tid + 256 * k;
+    const int j = tid + NTHR * k;
     if (j < nwords) dst[pos(j)] = (uint32_t)v[k];
   }
   return true;
@@ -97,100 +117,128 @@ struct HPos {
   }
 };
 
-__global__ void __launch_bounds__(256) k_decode_persistent(PersistArgs A) {
+// Role split inside a workgroup: on GFX9 a wavefront's memory counter retires
+// loads and stores in issue order, so a poll issued after a store waits for
+// that store's acknowledgement.  The last wave publishes each exchange (from
+// LDS) and the other waves poll, so pollers never have a store in flight.
+constexpr int PUB_WAVE = NWAVES - 1;
+constexpr int NPOLL = NT - 64;   // polling threads: waves 0 .. NWAVES-2
+
+__global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   __shared__ __align__(16) uint4 a_lds[DECODE_MAX_TOKENS][256];
   __shared__ float asum_lds[DECODE_MAX_TOKENS][64];
-  __shared__ __align__(16) float xstage[H];
   __shared__ float xown[DECODE_MAX_TOKENS][8];
-  __shared__ __align__(16) uint32_t zbuf[4][4 * E];   // per token: c[E] then s[E], fp64
+  __shared__ __align__(16) float xstage[H];
+  __shared__ __align__(16) uint32_t zbuf[4][4 * E];   // 4 tokens at a time: c[E] then s[E], fp64
   __shared__ __align__(16) float hbuf[HW];
+  // this workgroup's h values before publication: at most 2 D routed rows
+  // (D <= 16 * 6 distinct experts) times 16 tokens, plus 4 shared rows x 16
+  constexpr int HLOC = 2 * DECODE_MAX_TOKENS * TOPK * DECODE_MAX_TOKENS + 4 * DECODE_MAX_TOKENS;
+  __shared__ float hloc[HLOC];
+  __shared__ int hloc_idx[HLOC];
+  __shared__ int n_hloc;
+  __shared__ float xnew[DECODE_MAX_TOKENS][8];
   __shared__ int ids_l[DECODE_MAX_TOKENS][TOPK];
   __shared__ float w_l[DECODE_MAX_TOKENS][TOPK];
-  __shared__ int mark[E];
   __shared__ int list[DECODE_MAX_TOKENS * TOPK];
   __shared__ int wave_tot[4];
-  __shared__ signed char slotmap[DECODE_MAX_TOKENS * TOPK][DECODE_MAX_TOKENS];
-  __shared__ double red[4];
-  __shared__ double zpart[DECODE_MAX_TOKENS][4];
+  __shared__ double red[2][NWAVES];
+  __shared__ double zpart[DECODE_MAX_TOKENS][NWAVES];
+#ifdef FLINT_PHASE_TS
+  __shared__ unsigned long long ts_lds[TS_LAYERS][16];
+  __shared__ unsigned long long gts_lds[TS_LAYERS][4][4];
+#else
+  GtsLds gts_lds = nullptr;
+#endif
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int w = blockIdx.x;
   const int n = A.n;
+  const bool poller = wave != PUB_WAVE;
 
-  // P1 weights of the current layer, loaded one layer ahead
-  uint4 wr, cg, cu;
-  float sg, su, bw;
-  auto load_p1 = [&](const LayerW& L) {
-    wr = reinterpret_cast<const uint4*>(L.router + (size_t)w * H)[4 * lane + wave];
-    bw = L.bias[w];
-    const int r = w * 4 + wave;
-    cg = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)r * (H / 2))[lane];
-    cu = reinterpret_cast<const uint4*>(L.sh_up + (size_t)r * (H / 2))[lane];
-    sg = bf16_bits_to_f32(L.sh_gate_s[r * (H / G) + (lane >> 2)]);
-    su = bf16_bits_to_f32(L.sh_up_s[r * (H / G) + (lane >> 2)]);
+  // P1 weights (router part, shared gate/up row): the current layer's, and the
+  // next layer's loaded right after routing
+  struct P1W {
+    uint2 wr;
+    uint4 cg, cu;
+    float sg, su, bw;
   };
-  load_p1(layer_at(A.base, A.layer_stride, A.l0));
+  auto load_p1 = [&](const LayerW& L, P1W& p) {
+    p.wr = load_router_part(L.router + (size_t)w * H);
+    p.bw = L.bias[w];
+    if (wave < 4) {
+      const int r = w * 4 + wave;
+      p.cg = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)r * (H / 2))[lane];
+      p.cu = reinterpret_cast<const uint4*>(L.sh_up + (size_t)r * (H / 2))[lane];
+      p.sg = bf16_bits_to_f32(L.sh_gate_s[r * (H / G) + (lane >> 2)]);
+      p.su = bf16_bits_to_f32(L.sh_up_s[r * (H / G) + (lane >> 2)]);
+    }
+  };
+  P1W cur, nxt;
+  load_p1(layer_at(A.base, A.layer_stride, A.l0), cur);
+  nxt = cur;
   compiler_fence();
 
   for (int l = A.l0; l < A.l1; ++l) {
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
 
-    PHASE_MARK(0);
     // ---------------- P0: block input of every token
+    PHASE_MARK(0);
     for (int t = 0; t < n; ++t) {
       bool ok = true;
       if (l == A.l0) {
-        const float4* xs = reinterpret_cast<const float4*>(A.x + (size_t)t * H);
-        for (int j = tid; j < H / 4; j += 256) reinterpret_cast<float4*>(xstage)[j] = xs[j];
-      } else {
-        ok = gather<H / 256>(A.xx + (size_t)t * H, H, tag - 4 + 2, reinterpret_cast<uint32_t*>(xstage), A.err,
-                         Identity());
+        if (tid < H / 4) reinterpret_cast<float4*>(xstage)[tid] = reinterpret_cast<const float4*>(A.x + (size_t)t * H)[tid];
+      } else if (poller) {
+        ok = gather<(H + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xx + (size_t)t * H, H, tag - 4 + 2,
+                                                            reinterpret_cast<uint32_t*>(xstage), A.err, Identity(),
+                                                            tid, l, t == 0 ? 0 : -1, gts_lds);
       }
       if (__syncthreads_or(!ok)) return;
-      if (tid < 8) xown[t][tid] = xstage[8 * w + tid];
       if (t == 0) PHASE_MARK(1);
-      block_input_to_lds(xstage, a_lds[t], asum_lds[t], red);
-      __syncthreads();
+      const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
+      if ((tid >> 1) == w) {   // this workgroup's 8 output rows, kept for the residual
+        float* xo = xown[t] + 4 * (tid & 1);
+        xo[0] = xv.x; xo[1] = xv.y; xo[2] = xv.z; xo[3] = xv.w;
+      }
+      block_input(xv, reinterpret_cast<uint32_t*>(a_lds[t]), asum_lds[t], red[t & 1]);
+      __syncthreads();   // xstage is rewritten by the next token
     }
 
+    // ---------------- P1: router row w over all waves -> the publisher wave writes (c, s)
     PHASE_MARK(2);
-    // ---------------- P1: router row w (all four waves), then shared gate/up row 4 w + wave
     for (int t = 0; t < n; ++t) {
-      const double p = router_part(wr, a_lds[t]);
+      const double p = router_part(cur.wr, a_lds[t]);
       if (lane == 0) zpart[t][wave] = p;
     }
     __syncthreads();
-    if (tid < n) {
+    if (wave == PUB_WAVE && lane < n) {
+      const int t = lane;
       double sv, cv;
-      router_scores(zpart[tid], bw, sv, cv);
+      router_scores(zpart[t], cur.bw, sv, cv);
       const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
       const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
-      uint64_t* z = A.xz + (size_t)tid * 4 * E;
+      uint64_t* z = A.xz + (size_t)t * 4 * E;
       publish(z + 2 * w, tag, (uint32_t)cb);
       publish(z + 2 * w + 1, tag, (uint32_t)(cb >> 32));
       publish(z + 2 * E + 2 * w, tag, (uint32_t)sb);
       publish(z + 2 * E + 2 * w + 1, tag, (uint32_t)(sb >> 32));
     }
     PHASE_MARK(3);
-    {
-      const int r = w * 4 + wave;
-      for (int t = 0; t < n; ++t) {
-        const float hv = gateup_row_token(cg, sg, cu, su, a_lds[t], asum_lds[t][lane]);
-        if (lane == 0) publish(A.xh + (size_t)t * HW + TOPK * I + r, tag + 1, __float_as_uint(hv));
-      }
-    }
-
     PHASE_MARK(4);
+
     // ---------------- P2: routing, routed gate/up
-    mark[tid] = 0;
     for (int t0 = 0; t0 < n; t0 += 4) {
       const int nb = min(4, n - t0);
       for (int i = 0; i < nb; ++i) {
-        const bool ok = gather<4 * E / 256>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag, zbuf[i], A.err, Identity());
+        bool ok = true;
+        if (poller)
+          ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag,
+                                                                    zbuf[i], A.err, Identity(), tid, l,
+                                                                    (t0 + i == 0) ? 1 : -1, gts_lds);
         if (__syncthreads_or(!ok)) return;
-        if (t0 + i == 0) PHASE_MARK(5);
       }
+      PHASE_MARK(5);
       if (wave < nb) {
         const double* zc = reinterpret_cast<const double*>(zbuf[wave]);
         route_token(zc, zc + E, ids_l[t0 + wave], w_l[t0 + wave]);
@@ -198,83 +246,138 @@ __global__ void __launch_bounds__(256) k_decode_persistent(PersistArgs A) {
       __syncthreads();
     }
     PHASE_MARK(6);
-    if (w == 0 && A.trace_ids && tid < n * TOPK) {
-      const size_t o = (size_t)l * A.trace_cap * TOPK + tid;
-      A.trace_ids[o] = ids_l[tid / TOPK][tid % TOPK];
-      A.trace_w[o] = w_l[tid / TOPK][tid % TOPK];
+    if (w == 0 && A.trace_ids && wave == PUB_WAVE) {
+      for (int i = lane; i < n * TOPK; i += 64) {
+        const size_t o = (size_t)l * A.trace_cap * TOPK + i;
+        A.trace_ids[o] = ids_l[i / TOPK][i % TOPK];
+        A.trace_w[o] = w_l[i / TOPK][i % TOPK];
+      }
     }
-    if (tid < n * TOPK) mark[ids_l[tid / TOPK][tid % TOPK]] = 1;
-    __syncthreads();
-    const int D = distinct_experts(mark, list, wave_tot);
-    for (int i = tid; i < D * DECODE_MAX_TOKENS; i += 256)
-      slotmap[i / DECODE_MAX_TOKENS][i % DECODE_MAX_TOKENS] = -1;
-    __syncthreads();
-    if (tid < n * TOPK) slotmap[mark[ids_l[tid / TOPK][tid % TOPK]]][tid / TOPK] = (signed char)(tid % TOPK);
-    __syncthreads();
+    if (l + 1 < A.l1) load_p1(layer_at(A.base, A.layer_stride, l + 1), nxt);   // next layer's P1 weights
+    // distinct experts of the call (for one token: its six picks, in pick order)
+    const int D = (n == 1) ? TOPK : distinct_experts(ids_l, n, list, wave_tot);
+    const int* dl = (n == 1) ? ids_l[0] : list;
+    if (tid == 0) n_hloc = 0;
     PHASE_MARK(7);
+    // down codes of the first token for output row 8 w + wave: needed after the
+    // h exchange; loaded now so that nothing slow is in flight while polling
+    const int row = NWAVES * w + wave;
+    uint4 ca0, cb0;
+    float sa0, sb0;
+    load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
     {
-      // this wave's tasks q = w*4 + wave + k*NWG*4 over (distinct expert, row), loaded TB at a time
-      constexpr int TB = 4;
-      const int q0 = w * 4 + wave, nq = D * I;
-      for (int base = q0; base < nq; base += TB * NWG * 4) {
-        uint4 qg[TB], qu[TB];
-        float qsg[TB], qsu[TB];
+      // Row-pair tasks of this workgroup: 4 shared-expert rows (4 w .. 4 w + 3,
+      // weights prefetched) and R = 2 D routed rows (w R .. w R + R - 1 of the
+      // distinct experts' rows), dealt round-robin over the waves: local task j
+      // goes to wave j % 8; j < 4 are the shared rows.  Results go to LDS; the
+      // publisher wave writes them out after a barrier.
+      const int R = 2 * D;
+      constexpr int TB = 2;            // routed tasks a wave holds in flight
+      uint4 qg[TB], qu[TB];
+      float qsg[TB], qsu[TB];
+      auto load_batch = [&](int j0) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
-          const int q = base + b * NWG * 4;
-          if (q < nq) {
-            const size_t row = (size_t)list[q / I] * I + (q % I);
-            qg[b] = reinterpret_cast<const uint4*>(L.gate + row * (H / 2))[lane];
-            qu[b] = reinterpret_cast<const uint4*>(L.up + row * (H / 2))[lane];
-            qsg[b] = bf16_bits_to_f32(L.gate_s[row * (H / G) + (lane >> 2)]);
-            qsu[b] = bf16_bits_to_f32(L.up_s[row * (H / G) + (lane >> 2)]);
+          const int j = j0 + b * NWAVES;
+          if (j < 4 + R) {
+            const int q = w * R + (j - 4);
+            const size_t rr = (size_t)dl[q / I] * I + (q % I);
+            qg[b] = reinterpret_cast<const uint4*>(L.gate + rr * (H / 2))[lane];
+            qu[b] = reinterpret_cast<const uint4*>(L.up + rr * (H / 2))[lane];
+            qsg[b] = bf16_bits_to_f32(L.gate_s[rr * (H / G) + (lane >> 2)]);
+            qsu[b] = bf16_bits_to_f32(L.up_s[rr * (H / G) + (lane >> 2)]);
           }
         }
+      };
+      auto emit = [&](int word, float hv) {   // one h value of this workgroup, by lane 0
+        if (lane == 0) {
+          const int k = atomicAdd(&n_hloc, 1);   // < HLOC: see the bound above
+          hloc[k] = hv;
+          hloc_idx[k] = word;
+        }
+      };
+      auto compute_batch = [&](int j0) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
-          const int q = base + b * NWG * 4;
-          if (q >= nq) break;
-          const int d = q / I, r = q % I;
+          const int j = j0 + b * NWAVES;
+          if (j >= 4 + R) break;
+          const int q = w * R + (j - 4);
+          const int e = dl[q / I], r = q % I;
           for (int t = 0; t < n; ++t) {
-            const int slot = slotmap[d][t];
+            const int slot = slot_of(ids_l[t], e);
             if (slot < 0) continue;
-            const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds[t], asum_lds[t][lane]);
-            if (lane == 0) publish(A.xh + (size_t)t * HW + slot * I + r, tag + 1, __float_as_uint(hv));
+            emit(t * HW + slot * I + r, gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds[t], asum_lds[t][lane]));
           }
         }
+      };
+      __syncthreads();   // n_hloc reset visible
+      int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
+      load_batch(j0);
+      if (wave < 4) {   // the shared row (weights already here) while the routed loads fly
+        const int r = w * 4 + wave;
+        for (int t = 0; t < n; ++t)
+          emit(t * HW + TOPK * I + r, gateup_row_token(cur.cg, cur.sg, cur.cu, cur.su, a_lds[t], asum_lds[t][lane]));
+      }
+      compute_batch(j0);
+      for (j0 += TB * NWAVES; j0 < 4 + R; j0 += TB * NWAVES) {
+        load_batch(j0);
+        compute_batch(j0);
+      }
+    }
+    __syncthreads();
+    if (wave == PUB_WAVE) {
+      const int cnt = n_hloc;
+      for (int k = lane; k < cnt; k += 64) {
+        const int word = hloc_idx[k];
+        if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
+        else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     PHASE_MARK(8);
-    if (l + 1 < A.l1) load_p1(layer_at(A.base, A.layer_stride, l + 1));
-    compiler_fence();   // issue the next layer's loads now, before the waits below
 
-    // ---------------- P3: down rows 8 w + 2 wave + {0, 1} and combine
+    // ---------------- P3: down row 8 w + wave and combine, per token
     for (int t = 0; t < n; ++t) {
-      uint4 ca[2], cb[2];
-      float sa[2], sb[2];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) load_down_row(L, ids_l[t], 8 * w + 2 * wave + rr, ca[rr], sa[rr], cb[rr], sb[rr]);
-      compiler_fence();   // down codes in flight while waiting for h
-      const bool ok = gather<HW / 256>(A.xh + (size_t)t * HW, HW, tag + 1, reinterpret_cast<uint32_t*>(hbuf), A.err, HPos());
+      uint4 ca = ca0, cb = cb0;
+      float sa = sa0, sb = sb0;
+      if (t > 0) load_down_row(L, ids_l[t], row, ca, sa, cb, sb);
+      bool ok = true;
+      if (poller)
+        ok = gather<(HW + NPOLL - 1) / NPOLL, HPos, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
+                                                          reinterpret_cast<uint32_t*>(hbuf), A.err, HPos(), tid, l,
+                                                          t == 0 ? 2 : -1, gts_lds);
       if (__syncthreads_or(!ok)) return;
-      const int sub = lane & 15;
       if (t == 0) PHASE_MARK(9);
-      const HChunk ha = load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32);
-      const HChunk hb = (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
-                                    : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int row = 8 * w + 2 * wave + rr;
-        const float v = down_row_token(ca[rr], sa[rr], cb[rr], sb[rr], ha, hb, w_l[t], xown[t][row - 8 * w]);
-        if (lane == 0) {
-          if (l + 1 < A.l1) publish(A.xx + (size_t)t * H + row, tag + 2, __float_as_uint(v));
-          else A.out[(size_t)t * H + row] = v;
-        }
-      }
-      __syncthreads();
+      const int sub = lane & 15;
+      auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
+      auto load_b = [&] {
+        return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
+                           : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
+      };
+      const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l[t], xown[t][wave]);
+      if (lane == 0) xnew[t][wave] = v;
+      __syncthreads();   // hbuf is rewritten by the next token
     }
+    if (wave == PUB_WAVE) {
+      for (int i = lane; i < 8 * n; i += 64) {
+        const int t = i >> 3, r = NWAVES * w + (i & 7);
+        const float v = xnew[t][i & 7];
+        if (l + 1 < A.l1) publish(A.xx + (size_t)t * H + r, tag + 2, __float_as_uint(v));
+        else A.out[(size_t)t * H + r] = v;
+      }
+    }
+    cur = nxt;
     PHASE_MARK(10);
   }
+#ifdef FLINT_PHASE_TS
+  if (threadIdx.x == 0) {
+    for (int l = A.l0; l < A.l1 && l < TS_LAYERS; ++l) {
+      for (int k = 0; k < 16; ++k) g_phase_ts[l][k][blockIdx.x] = ts_lds[l][k];
+      if (blockIdx.x == 0)
+        for (int g = 0; g < 4; ++g)
+          for (int k = 0; k < 4; ++k) g_gather_ts[l][g][k] = gts_lds[l][g][k];
+    }
+  }
+#endif
 }
 
 __global__ void k_clear_words(uint64_t* p, size_t n) {
@@ -284,7 +387,7 @@ __global__ void k_clear_words(uint64_t* p, size_t n) {
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   PersistArgs a = args;
   void* kargs[] = {&a};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_decode_persistent), dim3(NWG), dim3(256), kargs,
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_decode_persistent), dim3(NWG), dim3(NT), kargs,
                                     0, s);
 }
 

@@ -32,16 +32,33 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
   return __uint_as_float(bits << 16);
 }
 
-// Round a double to bf16 with a single round-to-nearest-even: round to fp32
-// toward zero and make the result's last bit sticky ("round to odd"), then
-// round that fp32 to bf16 to nearest even.  fp32 carries 16 more significand
-// bits than bf16, so the two steps equal one direct rounding.
+// Round a double to bf16 with one round-to-nearest-even, with integer
+// operations on its bits (no rounding-mode changes).  Finite inputs only.
+// bf16 keeps 8 significant bits and fp32's exponent range; below 2^-126 the
+// spacing is 2^-133 (subnormals), handled with an exact power-of-two scaling.
 __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
-  float f = __double2float_rz(x);
-  uint32_t b = __float_as_uint(f);
-  if ((double)f != x) b |= 1u;
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return b >> 16;
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 63) << 15;
+  const int e11 = (int)((u >> 52) & 0x7FF);
+  if (e11 > 1023 - 127) {   // |x| >= 2^-126: normal bf16 (or rounds up into one)
+    const unsigned long long m = u & 0x7FFFFFFFFFFFFFFFull;
+    const unsigned long long r = m + 0xFFFFFFFFFFFull + ((m >> 45) & 1ull);   // RNE at bit 45
+    const uint32_t hi = (uint32_t)(r >> 45);            // exp11 (11 bits) | mant7
+    return sign | (uint32_t)(((hi >> 7) - (1023 - 127)) << 7) | (hi & 0x7F);
+  }
+  // |x| < 2^-126: multiple of 2^-133 nearest to |x|, ties to even (exact scaling)
+  const double q = rint(fabs(x) * 0x1p133);
+  return sign | (uint32_t)q;   // q <= 128; 128 is the smallest normal 0x0080
+}
+
+// True when x is within 8 fp64 units in the last place of a bf16 rounding
+// midpoint (or in the subnormal range), i.e. when a value known to within
+// 8 ulps of x might round differently from x.
+__device__ __forceinline__ bool near_bf16_midpoint(double x) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const int e11 = (int)((u >> 52) & 0x7FF);
+  const long long d = (long long)(u & 0x1FFFFFFFFFFFull) - (long long)0x100000000000ull;   // low 45 bits - half
+  return e11 <= 1023 - 127 || (d >= -8 && d <= 8);
 }
 
 // Position of element k of a 2048-wide activation in pair order.  Within each
