@@ -24,7 +24,7 @@ __global__ void __launch_bounds__(NT) k_norm_router(const float* __restrict__ x,
     const float4 xv = reinterpret_cast<const float4*>(x + (size_t)t * H)[tid];
     block_input(xv, reinterpret_cast<uint32_t*>(a_lds[t]), asum_lds[t], red[t & 1]);
   }
-  __syncthreads();
+  wg_sync();
   if (blockIdx.x == 0) {
     for (int t = 0; t < n; ++t) {
       if (tid < 256) reinterpret_cast<uint4*>(ws.a)[t * 256 + tid] = a_lds[t][tid];
@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(NT) k_norm_router(const float* __restrict__ x,
       if (lane == 0) zpart[t][wave] = p;
     }
   }
-  __syncthreads();
+  wg_sync();
   if (tid < n) {
     double s, c;
     router_scores(zpart[tid], L.bias[e], s, c);
@@ -50,8 +50,8 @@ __global__ void __launch_bounds__(NT) k_norm_router(const float* __restrict__ x,
     const int r = e * 4 + wave;
     const uint4 cg = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)r * (H / 2))[lane];
     const uint4 cu = reinterpret_cast<const uint4*>(L.sh_up + (size_t)r * (H / 2))[lane];
-    const float sg = bf16_bits_to_f32(L.sh_gate_s[r * (H / G) + (lane >> 2)]);
-    const float su = bf16_bits_to_f32(L.sh_up_s[r * (H / G) + (lane >> 2)]);
+    const uint32_t sg = L.sh_gate_s[r * (H / G) + (lane >> 2)];
+    const uint32_t su = L.sh_up_s[r * (H / G) + (lane >> 2)];
     for (int t = 0; t < n; ++t) {
       const float hv = gateup_row_token(cg, sg, cu, su, a_lds[t], asum_lds[t][lane]);
       if (lane == 0) ws.hsh[t * IS + r] = hv;
@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(NT) k_route_gateup(int n, LayerW L, DecodeWS w
     if (tid < 64) asum_lds[t][tid] = ws.asum[t * 64 + tid];
   }
   for (int t = wave; t < n; t += NWAVES) route_token(ws.c + t * E, ws.s + t * E, ids_l[t], w_l[t]);
-  __syncthreads();
+  wg_sync();
   if (blockIdx.x == 0 && tid < n * TOPK) {
     ws.ids[tid] = ids_l[tid / TOPK][tid % TOPK];
     ws.w[tid] = w_l[tid / TOPK][tid % TOPK];
@@ -89,8 +89,8 @@ __global__ void __launch_bounds__(NT) k_route_gateup(int n, LayerW L, DecodeWS w
     const size_t row = (size_t)e * I + r;
     const uint4 cg = reinterpret_cast<const uint4*>(L.gate + row * (H / 2))[lane];
     const uint4 cu = reinterpret_cast<const uint4*>(L.up + row * (H / 2))[lane];
-    const float sg = bf16_bits_to_f32(L.gate_s[row * (H / G) + (lane >> 2)]);
-    const float su = bf16_bits_to_f32(L.up_s[row * (H / G) + (lane >> 2)]);
+    const uint32_t sg = L.gate_s[row * (H / G) + (lane >> 2)];
+    const uint32_t su = L.up_s[row * (H / G) + (lane >> 2)];
     for (int t = 0; t < n; ++t) {
       const int slot = slot_of(ids_l[t], e);
       if (slot < 0) continue;
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(NT) k_down_combine(const float* xin, float* ou
   const int nrow = blockIdx.x * NWAVES + wave;
   for (int t = 0; t < n; ++t) {
     uint4 ca, cb;
-    float sa, sb;
+    uint32_t sa, sb;
     load_down_row(L, ws.ids + t * TOPK, nrow, ca, sa, cb, sb);
     const float* h = ws.h + (size_t)t * TOPK * I;
     const float* hs = ws.hsh + (size_t)t * IS;

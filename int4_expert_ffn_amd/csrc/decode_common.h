@@ -27,23 +27,38 @@ __device__ __forceinline__ void block_input(float4 xv, uint32_t* a_u32, float* a
   for (int j = 0; j < 4; ++j) ss += xs[j] * xs[j];
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
-  __syncthreads();
+  wg_sync();
   double tot = red[0];
 #pragma unroll
   for (int i = 1; i < NWAVES; ++i) tot += red[i];
   const double ms = tot / (double)H + RMS_EPS;
   const double rinv = rsqrt(ms);
-  uint32_t b[4];
-  float part = 0.f;
+  double q[4];
+  float qf[4];
+  bool hard = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    // x * rsqrt(ms) is within a few fp64 ulps of x / sqrt(ms); where that
-    // could change the bf16 rounding, use the correctly rounded quotient
-    double q = xs[j] * rinv;
-    if (near_bf16_midpoint(q)) q = xs[j] / sqrt(ms);
-    b[j] = f64_to_bf16_rne(q);
-    part += bf16_bits_to_f32(b[j]);
+    q[j] = xs[j] * rinv;
+    qf[j] = (float)q[j];
+    hard |= f32_on_bf16_midpoint(qf[j]);
   }
+  uint32_t b[4];
+  if (__builtin_expect(__ballot(hard) != 0ull, 0)) {   // wave-uniform, rare
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // x * rsqrt(ms) is within a few fp64 ulps of x / sqrt(ms); where that
+      // could change the bf16 rounding, use the correctly rounded quotient
+      double qq = q[j];
+      if (near_bf16_midpoint(qq)) qq = xs[j] / sqrt(ms);
+      b[j] = f64_to_bf16_rne(qq);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = f32_to_bf16_rne(qf[j]);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) part += bf16_bits_to_f32(b[j]);
   const int c = tid >> 1, half = tid & 1;
   const int P = ((c & 3) * 64 + (c >> 2)) * 4;
   a_u32[P + half] = b[0] | (b[2] << 16);       // (k0,k2) or (k4,k6)
@@ -197,13 +212,17 @@ __device__ __forceinline__ void route_token(const double* __restrict__ c, const 
 }
 
 // ----------------------------------------------------------------- gate / up
+// Scales are passed as raw bf16 bits and widened where they are used: a
+// conversion next to the load would make the wave wait for that load (and,
+// the memory counter being in order, for every load issued before it).
+
 // gate/up of one row for one token: returns h = silu(g) u (same in all lanes)
-__device__ __forceinline__ float gateup_row_token(uint4 cg, float sg, uint4 cu, float su, const uint4* a_tok,
-                                                  float asum_lane) {
+__device__ __forceinline__ float gateup_row_token(uint4 cg, uint32_t sg_bits, uint4 cu, uint32_t su_bits,
+                                                  const uint4* a_tok, float asum_lane) {
   const int lane = threadIdx.x & 63;
   const uint4 av[4] = {a_tok[lane], a_tok[64 + lane], a_tok[128 + lane], a_tok[192 + lane]};
-  const float g = wave_sum(lane_dot_gateup(cg, av, asum_lane, sg));
-  const float u = wave_sum(lane_dot_gateup(cu, av, asum_lane, su));
+  const float g = wave_sum(lane_dot_gateup(cg, av, asum_lane, bf16_bits_to_f32(sg_bits)));
+  const float u = wave_sum(lane_dot_gateup(cu, av, asum_lane, bf16_bits_to_f32(su_bits)));
   return silu_mul(g, u);
 }
 
@@ -246,18 +265,18 @@ __device__ __forceinline__ int transposed_pos(int k, int nsub) {
   return ((((k & 31) >> 2) * nsub + (k >> 5)) << 2) | (k & 3);
 }
 
-// Codes and scale of lane `sub` of down row `row` of a [rows][K] int4 matrix.
+// Codes and scale bits of lane `sub` of down row `row` of a [rows][K] int4 matrix.
 __device__ __forceinline__ void load_down_lane(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                               int K, int row, int sub, uint4& c, float& sc) {
+                                               int K, int row, int sub, uint4& c, uint32_t& sc) {
   c = reinterpret_cast<const uint4*>(codes + (size_t)row * (K / 2))[sub];
-  sc = bf16_bits_to_f32(scales[(size_t)row * (K / G) + (sub >> 2)]);
+  sc = scales[(size_t)row * (K / G) + (sub >> 2)];
 }
 
 // This lane's down codes for output row `row` of one token:
 //   pass A: lanes 16 s .. 16 s + 15 take routed slot s (s = 0..3)
 //   pass B: lanes 0..31 take slots 4, 5; lanes 32..63 the shared expert.
-__device__ __forceinline__ void load_down_row(const LayerW& L, const int* ids, int row, uint4& ca, float& sa,
-                                              uint4& cb, float& sb) {
+__device__ __forceinline__ void load_down_row(const LayerW& L, const int* ids, int row, uint4& ca, uint32_t& sa,
+                                              uint4& cb, uint32_t& sb) {
   const int lane = threadIdx.x & 63, sub = lane & 15;
   const int e_a = ids[lane >> 4];
   load_down_lane(L.down + (size_t)e_a * H * (I / 2), L.down_s + (size_t)e_a * H * (I / G), I, row, sub, ca, sa);
@@ -276,16 +295,16 @@ __device__ __forceinline__ void load_down_row(const LayerW& L, const int* ids, i
 // on 32..63); they are called one after the other so only one chunk is live.
 // The result is the same in every lane.
 template <typename LoadA, typename LoadB>
-__device__ __forceinline__ float down_row_token(uint4 ca, float sa, uint4 cb, float sb, LoadA load_a, LoadB load_b,
-                                                const float* w, float xres) {
+__device__ __forceinline__ float down_row_token(uint4 ca, uint32_t sa, uint4 cb, uint32_t sb, LoadA load_a,
+                                                LoadB load_b, const float* w, float xres) {
   float ya, yb;
   {
     const HChunk ha = load_a();
-    ya = row16_sum(lane_dot_down(ca, ha.v, ha.sum, sa));
+    ya = row16_sum(lane_dot_down(ca, ha.v, ha.sum, bf16_bits_to_f32(sa)));
   }
   {
     const HChunk hb = load_b();
-    yb = row16_sum(lane_dot_down(cb, hb.v, hb.sum, sb));
+    yb = row16_sum(lane_dot_down(cb, hb.v, hb.sum, bf16_bits_to_f32(sb)));
   }
   const float ysh = lane_bcast(yb + dpp_f32<DPP_BCAST15, 0x8>(yb), 63);   // rows 2 + 3: shared row
   const float y0 = lane_bcast(ya, 0), y1 = lane_bcast(ya, 16), y2 = lane_bcast(ya, 32), y3 = lane_bcast(ya, 48);
@@ -309,7 +328,7 @@ __device__ __forceinline__ int distinct_experts(const int (*ids)[TOPK], int n, i
     for (int i = 0; i < n * TOPK; ++i) f |= (ids[i / TOPK][i % TOPK] == tid);
   const unsigned long long bal = __ballot(f);
   if (lane == 0 && wave < E / 64) wave_tot[wave] = __popcll(bal);
-  __syncthreads();
+  wg_sync();
   if (f) {
     int off = __popcll(bal & ((1ull << lane) - 1ull));
     for (int i = 0; i < wave; ++i) off += wave_tot[i];
@@ -318,7 +337,7 @@ __device__ __forceinline__ int distinct_experts(const int (*ids)[TOPK], int n, i
   int D = 0;
 #pragma unroll
   for (int i = 0; i < E / 64; ++i) D += wave_tot[i];
-  __syncthreads();
+  wg_sync();
   return D;
 }
 

@@ -38,6 +38,8 @@ __device__ unsigned long long g_phase_ts[TS_LAYERS][16][NWG];
 __device__ unsigned long long g_gather_ts[TS_LAYERS][4][4];
 #define PHASE_MARK(k) \
   do { if (threadIdx.x == 0 && l < TS_LAYERS) ts_lds[l][k] = wall_clock64(); } while (0)
+#define PUB_MARK(k) \
+  do { if (threadIdx.x == 64 * PUB_WAVE && l < TS_LAYERS) ts_lds[l][k] = wall_clock64(); } while (0)
 #define GATHER_PROBE(slot, v) \
   do { if (threadIdx.x == 0 && dbg_id >= 0 && dbg_layer < TS_LAYERS) gts_lds[dbg_layer][dbg_id][slot] = (v); } while (0)
 extern "C" int flint_moe_debug_phase_ts(unsigned long long* host) {
@@ -48,6 +50,7 @@ extern "C" int flint_moe_debug_gather_ts(unsigned long long* host) {
 }
 #else
 #define PHASE_MARK(k) do { } while (0)
+#define PUB_MARK(k) do { } while (0)
 #define GATHER_PROBE(slot, v) do { } while (0)
 #endif
 
@@ -128,9 +131,23 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   __shared__ __align__(16) uint4 a_lds[DECODE_MAX_TOKENS][256];
   __shared__ float asum_lds[DECODE_MAX_TOKENS][64];
   __shared__ float xown[DECODE_MAX_TOKENS][8];
-  __shared__ __align__(16) float xstage[H];
-  __shared__ __align__(16) uint32_t zbuf[4][4 * E];   // 4 tokens at a time: c[E] then s[E], fp64
-  __shared__ __align__(16) float hbuf[HW];
+  // gather destination, shared by the three exchanges of a layer (their
+  // contents are never live together): x of one token [H], (c, s) of 4
+  // tokens [4][4 E] as fp64 halves, h of one token [HW] in transposed order
+  __shared__ __align__(16) uint32_t stage[HW];
+  float* const xstage = reinterpret_cast<float*>(stage);
+  uint32_t (*const zbuf)[4 * E] = reinterpret_cast<uint32_t (*)[4 * E]>(stage);
+  float* const hbuf = reinterpret_cast<float*>(stage);
+  static_assert(H <= HW && 4 * 4 * E <= HW, "gather staging too small");
+  // This workgroup's P1 weights of the current layer: router row w, one uint2
+  // per thread in the order router_part() takes them; shared-expert gate and
+  // up rows 4 w + v (v < 4), one uint4 per lane, with their scale bits; and
+  // bias[w].  The publisher wave fills it for the next layer while the other
+  // waves gather h.
+  __shared__ uint2 p1_router[NT];
+  __shared__ uint4 p1_code[4][2][64];
+  __shared__ uint16_t p1_scale[4][2][H / G];
+  __shared__ float p1_bias;
   // this workgroup's h values before publication: at most 2 D routed rows
   // (D <= 16 * 6 distinct experts) times 16 tokens, plus 4 shared rows x 16
   constexpr int HLOC = 2 * DECODE_MAX_TOKENS * TOPK * DECODE_MAX_TOKENS + 4 * DECODE_MAX_TOKENS;
@@ -151,33 +168,71 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   GtsLds gts_lds = nullptr;
 #endif
 
+  __shared__ int bail[2];
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int w = blockIdx.x;
   const int n = A.n;
   const bool poller = wave != PUB_WAVE;
 
-  // P1 weights (router part, shared gate/up row): the current layer's, and the
-  // next layer's loaded right after routing
-  struct P1W {
-    uint2 wr;
-    uint4 cg, cu;
-    float sg, su, bw;
+  // Barrier that also tells every wave whether any thread timed out.  The
+  // flags are sticky and used alternately: the reads after one such barrier
+  // all happen before the next one, which is the earliest a thread can set the
+  // other flag, so no read can see a later call's failure.
+  if (tid < 2) bail[tid] = 0;
+  int bail_par = 0;
+  auto sync_or = [&](bool fail) {
+    if (fail) bail[bail_par] = 1;
+    wg_sync();
+    const bool r = bail[bail_par] != 0;
+    bail_par ^= 1;
+    return r;
   };
-  auto load_p1 = [&](const LayerW& L, P1W& p) {
-    p.wr = load_router_part(L.router + (size_t)w * H);
-    p.bw = L.bias[w];
-    if (wave < 4) {
-      const int r = w * 4 + wave;
-      p.cg = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)r * (H / 2))[lane];
-      p.cu = reinterpret_cast<const uint4*>(L.sh_up + (size_t)r * (H / 2))[lane];
-      p.sg = bf16_bits_to_f32(L.sh_gate_s[r * (H / G) + (lane >> 2)]);
-      p.su = bf16_bits_to_f32(L.sh_up_s[r * (H / G) + (lane >> 2)]);
+  wg_sync();
+
+  // P1 weights of one layer in flight in the publisher wave's registers
+  struct P1Stage {
+    uint4 r[4], c[8];
+    uint32_t sg, su;
+    float b;
+  };
+  auto p1_issue = [&](const LayerW& L, P1Stage& q) {
+    const uint4* rr = reinterpret_cast<const uint4*>(L.router + (size_t)w * H);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q.r[k] = rr[64 * k + lane];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      q.c[2 * v] = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)(4 * w + v) * (H / 2))[lane];
+      q.c[2 * v + 1] = reinterpret_cast<const uint4*>(L.sh_up + (size_t)(4 * w + v) * (H / 2))[lane];
     }
+    q.sg = L.sh_gate_s[(size_t)4 * w * (H / G) + lane];   // rows 4 w .. 4 w + 3, 16 scales each
+    q.su = L.sh_up_s[(size_t)4 * w * (H / G) + lane];
+    q.b = L.bias[w];
   };
-  P1W cur, nxt;
-  load_p1(layer_at(A.base, A.layer_stride, A.l0), cur);
-  nxt = cur;
-  compiler_fence();
+  auto p1_write = [&](const P1Stage& q) {
+    // uint2 g of the router row goes to the thread that load_router_part()
+    // gives it: g = 2 (4 lane + (wave & 3)) + (wave >> 2)
+    auto slot = [](int g) { return ((((g & 1) << 2) | ((g & 7) >> 1)) << 6) | (g >> 3); };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 64 * k + lane;
+      p1_router[slot(2 * i)] = make_uint2(q.r[k].x, q.r[k].y);
+      p1_router[slot(2 * i + 1)] = make_uint2(q.r[k].z, q.r[k].w);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p1_code[v][0][lane] = q.c[2 * v];
+      p1_code[v][1][lane] = q.c[2 * v + 1];
+    }
+    p1_scale[lane >> 4][0][lane & 15] = (uint16_t)q.sg;
+    p1_scale[lane >> 4][1][lane & 15] = (uint16_t)q.su;
+    if (lane == 0) p1_bias = q.b;
+  };
+  if (wave == PUB_WAVE) {
+    P1Stage q;
+    p1_issue(layer_at(A.base, A.layer_stride, A.l0), q);
+    p1_write(q);
+  }
 
   for (int l = A.l0; l < A.l1; ++l) {
     const LayerW L = layer_at(A.base, A.layer_stride, l);
@@ -194,7 +249,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
                                                             reinterpret_cast<uint32_t*>(xstage), A.err, Identity(),
                                                             tid, l, t == 0 ? 0 : -1, gts_lds);
       }
-      if (__syncthreads_or(!ok)) return;
+      if (sync_or(!ok)) return;
       if (t == 0) PHASE_MARK(1);
       const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
       if ((tid >> 1) == w) {   // this workgroup's 8 output rows, kept for the residual
@@ -202,20 +257,21 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         xo[0] = xv.x; xo[1] = xv.y; xo[2] = xv.z; xo[3] = xv.w;
       }
       block_input(xv, reinterpret_cast<uint32_t*>(a_lds[t]), asum_lds[t], red[t & 1]);
-      __syncthreads();   // xstage is rewritten by the next token
+      wg_sync();   // xstage is rewritten by the next token
     }
 
     // ---------------- P1: router row w over all waves -> the publisher wave writes (c, s)
     PHASE_MARK(2);
     for (int t = 0; t < n; ++t) {
-      const double p = router_part(cur.wr, a_lds[t]);
+      const double p = router_part(p1_router[tid], a_lds[t]);
       if (lane == 0) zpart[t][wave] = p;
     }
-    __syncthreads();
+    wg_sync();
+    PUB_MARK(11);
     if (wave == PUB_WAVE && lane < n) {
       const int t = lane;
       double sv, cv;
-      router_scores(zpart[t], cur.bw, sv, cv);
+      router_scores(zpart[t], p1_bias, sv, cv);
       const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
       const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
       uint64_t* z = A.xz + (size_t)t * 4 * E;
@@ -224,6 +280,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       publish(z + 2 * E + 2 * w, tag, (uint32_t)sb);
       publish(z + 2 * E + 2 * w + 1, tag, (uint32_t)(sb >> 32));
     }
+    PUB_MARK(12);
     PHASE_MARK(3);
     PHASE_MARK(4);
 
@@ -236,14 +293,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
           ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag,
                                                                     zbuf[i], A.err, Identity(), tid, l,
                                                                     (t0 + i == 0) ? 1 : -1, gts_lds);
-        if (__syncthreads_or(!ok)) return;
+        if (sync_or(!ok)) return;
       }
       PHASE_MARK(5);
       if (wave < nb) {
         const double* zc = reinterpret_cast<const double*>(zbuf[wave]);
         route_token(zc, zc + E, ids_l[t0 + wave], w_l[t0 + wave]);
       }
-      __syncthreads();
+      wg_sync();
     }
     PHASE_MARK(6);
     if (w == 0 && A.trace_ids && wave == PUB_WAVE) {
@@ -253,7 +310,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         A.trace_w[o] = w_l[i / TOPK][i % TOPK];
       }
     }
-    if (l + 1 < A.l1) load_p1(layer_at(A.base, A.layer_stride, l + 1), nxt);   // next layer's P1 weights
     // distinct experts of the call (for one token: its six picks, in pick order)
     const int D = (n == 1) ? TOPK : distinct_experts(ids_l, n, list, wave_tot);
     const int* dl = (n == 1) ? ids_l[0] : list;
@@ -263,7 +319,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     // h exchange; loaded now so that nothing slow is in flight while polling
     const int row = NWAVES * w + wave;
     uint4 ca0, cb0;
-    float sa0, sb0;
+    uint32_t sa0, sb0;
     load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
     {
       // Row-pair tasks of this workgroup: 4 shared-expert rows (4 w .. 4 w + 3,
@@ -274,7 +330,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       const int R = 2 * D;
       constexpr int TB = 2;            // routed tasks a wave holds in flight
       uint4 qg[TB], qu[TB];
-      float qsg[TB], qsu[TB];
+      uint32_t qsg[TB], qsu[TB];
       auto load_batch = [&](int j0) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
@@ -284,8 +340,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
             const size_t rr = (size_t)dl[q / I] * I + (q % I);
             qg[b] = reinterpret_cast<const uint4*>(L.gate + rr * (H / 2))[lane];
             qu[b] = reinterpret_cast<const uint4*>(L.up + rr * (H / 2))[lane];
-            qsg[b] = bf16_bits_to_f32(L.gate_s[rr * (H / G) + (lane >> 2)]);
-            qsu[b] = bf16_bits_to_f32(L.up_s[rr * (H / G) + (lane >> 2)]);
+            qsg[b] = L.gate_s[rr * (H / G) + (lane >> 2)];
+            qsu[b] = L.up_s[rr * (H / G) + (lane >> 2)];
           }
         }
       };
@@ -310,13 +366,15 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
           }
         }
       };
-      __syncthreads();   // n_hloc reset visible
+      wg_sync();   // n_hloc reset visible
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
       if (wave < 4) {   // the shared row (weights already here) while the routed loads fly
         const int r = w * 4 + wave;
         for (int t = 0; t < n; ++t)
-          emit(t * HW + TOPK * I + r, gateup_row_token(cur.cg, cur.sg, cur.cu, cur.su, a_lds[t], asum_lds[t][lane]));
+          emit(t * HW + TOPK * I + r, gateup_row_token(p1_code[wave][0][lane], p1_scale[wave][0][lane >> 2],
+                                                       p1_code[wave][1][lane], p1_scale[wave][1][lane >> 2], a_lds[t],
+                                                       asum_lds[t][lane]));
       }
       compute_batch(j0);
       for (j0 += TB * NWAVES; j0 < 4 + R; j0 += TB * NWAVES) {
@@ -324,7 +382,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         compute_batch(j0);
       }
     }
-    __syncthreads();
+    wg_sync();
+    PUB_MARK(13);
     if (wave == PUB_WAVE) {
       const int cnt = n_hloc;
       for (int k = lane; k < cnt; k += 64) {
@@ -332,20 +391,28 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      // the next layer's P1 weights: this layer's were last read by the
+      // shared rows above; the other waves gather h meanwhile
+      if (l + 1 < A.l1) {
+        P1Stage q;
+        p1_issue(layer_at(A.base, A.layer_stride, l + 1), q);
+        p1_write(q);
+      }
     }
+    PUB_MARK(14);
     PHASE_MARK(8);
 
     // ---------------- P3: down row 8 w + wave and combine, per token
     for (int t = 0; t < n; ++t) {
       uint4 ca = ca0, cb = cb0;
-      float sa = sa0, sb = sb0;
+      uint32_t sa = sa0, sb = sb0;
       if (t > 0) load_down_row(L, ids_l[t], row, ca, sa, cb, sb);
       bool ok = true;
       if (poller)
         ok = gather<(HW + NPOLL - 1) / NPOLL, HPos, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
                                                           reinterpret_cast<uint32_t*>(hbuf), A.err, HPos(), tid, l,
                                                           t == 0 ? 2 : -1, gts_lds);
-      if (__syncthreads_or(!ok)) return;
+      if (sync_or(!ok)) return;
       if (t == 0) PHASE_MARK(9);
       const int sub = lane & 15;
       auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
@@ -355,7 +422,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       };
       const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l[t], xown[t][wave]);
       if (lane == 0) xnew[t][wave] = v;
-      __syncthreads();   // hbuf is rewritten by the next token
+      wg_sync();   // hbuf is rewritten by the next token
     }
     if (wave == PUB_WAVE) {
       for (int i = lane; i < 8 * n; i += 64) {
@@ -365,7 +432,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         else A.out[(size_t)t * H + r] = v;
       }
     }
-    cur = nxt;
+    PUB_MARK(15);
     PHASE_MARK(10);
   }
 #ifdef FLINT_PHASE_TS

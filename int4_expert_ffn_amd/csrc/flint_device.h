@@ -61,6 +61,21 @@ __device__ __forceinline__ bool near_bf16_midpoint(double x) {
   return e11 <= 1023 - 127 || (d >= -8 && d <= 8);
 }
 
+// bf16 bits of an fp32 value, rounded to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Rounding fp64 -> fp32 -> bf16 (both to nearest even) gives the bf16 nearest
+// to x except when the fp32 value is itself a bf16 midpoint (low 16 bits
+// 0x8000).  That test also holds whenever x lies within 8 fp64 ulps of a
+// midpoint (the fp32 rounding of such an x is the midpoint), so a false
+// result here implies a false near_bf16_midpoint(x) outside the subnormal
+// range, and there the two roundings agree as well.
+__device__ __forceinline__ bool f32_on_bf16_midpoint(float f) {
+  return (__float_as_uint(f) & 0xFFFFu) == 0x8000u;
+}
+
 // Position of element k of a 2048-wide activation in pair order.  Within each
 // 8-element chunk the order is (0, 2, 4, 6, 1, 3, 5, 7): the even elements are
 // the low nibbles of a code dword, the odd ones the high nibbles.
@@ -151,6 +166,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // Keep the compiler from moving memory operations across this point (used to
 // issue prefetch loads before a wait loop).  Emits no instruction.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also orders global
+// memory, so each wave first waits for the acknowledgement of every store it
+// has in flight; stores that are written through to device memory take
+// microseconds to acknowledge.  No kernel here passes data between waves of
+// one workgroup through global memory, so the LDS fences suffice.
+__device__ __forceinline__ void wg_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ------------------------------------------------------------------ int4 dots
 // One code dword holds 8 nibbles (k0..k7).  After xor 0x88888888 each nibble
