@@ -69,21 +69,20 @@ __device__ __forceinline__ void block_input(float4 xv, uint32_t* a_u32, float* a
   if ((tid & 7) == 0) asum_lds[tid >> 3] = part;
 }
 
-// The router row of expert e is split over the 8 waves of a workgroup: lane L
-// of wave v holds the row's 4 weights (8 bytes) for elements 4 (v >> 2) ..
-// 4 (v >> 2) + 3 of 8-element chunk 4 L + (v & 3).
+// The router row of expert e is split over the 512 threads of a workgroup:
+// thread t holds the row's 4 weights (8 bytes) for elements 4 t .. 4 t + 3,
+// i.e. half t & 1 of 8-element chunk t >> 1.
 __device__ __forceinline__ uint2 load_router_part(const uint16_t* router_row) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return reinterpret_cast<const uint2*>(router_row)[2 * (4 * lane + (wave & 3)) + (wave >> 2)];
+  return reinterpret_cast<const uint2*>(router_row)[threadIdx.x];
 }
 
 // This wave's part of the router logit (fp64, same value in every lane).
 __device__ __forceinline__ double router_part(uint2 w, const uint4* a_tok) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint4 a = a_tok[(wave & 3) * 64 + lane];
+  const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const uint4 a = a_tok[(c & 3) * 64 + (c >> 2)];
   // weights in natural order k0..k3 of the half; activations in pair order
-  const uint32_t alo = (wave >> 2) ? a.y : a.x;   // (k0,k2) or (k4,k6)
-  const uint32_t ahi = (wave >> 2) ? a.w : a.z;   // (k1,k3) or (k5,k7)
+  const uint32_t alo = half ? a.y : a.x;   // (k0,k2) or (k4,k6)
+  const uint32_t ahi = half ? a.w : a.z;   // (k1,k3) or (k5,k7)
   const float wk[4] = {bf16_bits_to_f32(w.x & 0xFFFF), bf16_bits_to_f32(w.x >> 16),
                        bf16_bits_to_f32(w.y & 0xFFFF), bf16_bits_to_f32(w.y >> 16)};
   const float ak[4] = {bf16_bits_to_f32(alo & 0xFFFF), bf16_bits_to_f32(ahi & 0xFFFF),

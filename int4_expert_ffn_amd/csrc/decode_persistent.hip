@@ -120,6 +120,21 @@ struct HPos {
   }
 };
 
+// Asynchronous copy of 16 (or 4) bytes per lane from global memory into LDS:
+// lane i's bytes land at lds + i * size.  Completion is counted by the
+// wave's memory counter like a load; nothing is written to registers.
+typedef __attribute__((address_space(1))) void gmem_void;
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void copy_to_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gmem_void*)src, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void copy_to_lds4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gmem_void*)src, (lds_void*)lds, 4, 0, 0);
+}
+
+// Wait until every memory operation this wave has issued is complete.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
 // Role split inside a workgroup: on GFX9 a wavefront's memory counter retires
 // loads and stores in issue order, so a poll issued after a store waits for
 // that store's acknowledgement.  The last wave publishes each exchange (from
@@ -139,15 +154,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   uint32_t (*const zbuf)[4 * E] = reinterpret_cast<uint32_t (*)[4 * E]>(stage);
   float* const hbuf = reinterpret_cast<float*>(stage);
   static_assert(H <= HW && 4 * 4 * E <= HW, "gather staging too small");
-  // This workgroup's P1 weights of the current layer: router row w, one uint2
-  // per thread in the order router_part() takes them; shared-expert gate and
-  // up rows 4 w + v (v < 4), one uint4 per lane, with their scale bits; and
-  // bias[w].  The publisher wave fills it for the next layer while the other
-  // waves gather h.
-  __shared__ uint2 p1_router[NT];
-  __shared__ uint4 p1_code[4][2][64];
-  __shared__ uint16_t p1_scale[4][2][H / G];
-  __shared__ float p1_bias;
+  // This workgroup's P1 weights, copied from global memory by the publisher
+  // wave: router row w (uint2 t for thread t) and bias[w] of the current
+  // layer; shared-expert gate (g = 0) and up (g = 1) rows 4 w + v, v < 4
+  // (uint4 per lane) with their 16 scales each, for layer l in buffer l & 1.
+  // The next layer's copy is issued right after this layer's (c, s) are
+  // published: the router row and bias have been used by then, and the other
+  // shared-row buffer is free.  It completes while the (c, s) are gathered.
+  __shared__ __align__(16) uint2 p1_router[NT];
+  __shared__ __align__(16) uint4 p1_code[2][2][4][64];
+  __shared__ __align__(16) uint16_t p1_scale[2][2][4 * (H / G)];
+  __shared__ __align__(16) float p1_bias;
   // this workgroup's h values before publication: at most 2 D routed rows
   // (D <= 16 * 6 distinct experts) times 16 tokens, plus 4 shared rows x 16
   constexpr int HLOC = 2 * DECODE_MAX_TOKENS * TOPK * DECODE_MAX_TOKENS + 4 * DECODE_MAX_TOKENS;
@@ -190,48 +207,26 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   };
   wg_sync();
 
-  // P1 weights of one layer in flight in the publisher wave's registers
-  struct P1Stage {
-    uint4 r[4], c[8];
-    uint32_t sg, su;
-    float b;
-  };
-  auto p1_issue = [&](const LayerW& L, P1Stage& q) {
+  // publisher wave: copy layer l's P1 weights into LDS (14 instructions)
+  auto p1_copy = [&](int l) {
+    const LayerW L = layer_at(A.base, A.layer_stride, l);
+    const int b = l & 1;
     const uint4* rr = reinterpret_cast<const uint4*>(L.router + (size_t)w * H);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q.r[k] = rr[64 * k + lane];
+    for (int k = 0; k < 4; ++k) copy_to_lds16(rr + 64 * k + lane, reinterpret_cast<uint4*>(p1_router) + 64 * k);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      q.c[2 * v] = reinterpret_cast<const uint4*>(L.sh_gate + (size_t)(4 * w + v) * (H / 2))[lane];
-      q.c[2 * v + 1] = reinterpret_cast<const uint4*>(L.sh_up + (size_t)(4 * w + v) * (H / 2))[lane];
+      copy_to_lds16(reinterpret_cast<const uint4*>(L.sh_gate + (size_t)(4 * w + v) * (H / 2)) + lane, p1_code[b][0][v]);
+      copy_to_lds16(reinterpret_cast<const uint4*>(L.sh_up + (size_t)(4 * w + v) * (H / 2)) + lane, p1_code[b][1][v]);
     }
-    q.sg = L.sh_gate_s[(size_t)4 * w * (H / G) + lane];   // rows 4 w .. 4 w + 3, 16 scales each
-    q.su = L.sh_up_s[(size_t)4 * w * (H / G) + lane];
-    q.b = L.bias[w];
-  };
-  auto p1_write = [&](const P1Stage& q) {
-    // uint2 g of the router row goes to the thread that load_router_part()
-    // gives it: g = 2 (4 lane + (wave & 3)) + (wave >> 2)
-    auto slot = [](int g) { return ((((g & 1) << 2) | ((g & 7) >> 1)) << 6) | (g >> 3); };
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = 64 * k + lane;
-      p1_router[slot(2 * i)] = make_uint2(q.r[k].x, q.r[k].y);
-      p1_router[slot(2 * i + 1)] = make_uint2(q.r[k].z, q.r[k].w);
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      p1_code[v][0][lane] = q.c[2 * v];
-      p1_code[v][1][lane] = q.c[2 * v + 1];
-    }
-    p1_scale[lane >> 4][0][lane & 15] = (uint16_t)q.sg;
-    p1_scale[lane >> 4][1][lane & 15] = (uint16_t)q.su;
-    if (lane == 0) p1_bias = q.b;
+    // scales of rows 4 w .. 4 w + 3: gate on lanes 0..31, up on 32..63 (two per lane)
+    const uint16_t* sc = (lane < 32 ? L.sh_gate_s : L.sh_up_s) + (size_t)4 * w * (H / G) + 2 * (lane & 31);
+    copy_to_lds4(sc, p1_scale[b]);
+    if (lane == 0) copy_to_lds4(L.bias + w, &p1_bias);
   };
   if (wave == PUB_WAVE) {
-    P1Stage q;
-    p1_issue(layer_at(A.base, A.layer_stride, A.l0), q);
-    p1_write(q);
+    p1_copy(A.l0);
+    wait_all_memory();
   }
 
   for (int l = A.l0; l < A.l1; ++l) {
@@ -279,6 +274,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       publish(z + 2 * w + 1, tag, (uint32_t)(cb >> 32));
       publish(z + 2 * E + 2 * w, tag, (uint32_t)sb);
       publish(z + 2 * E + 2 * w + 1, tag, (uint32_t)(sb >> 32));
+    }
+    if (wave == PUB_WAVE && l + 1 < A.l1) {
+      p1_copy(l + 1);
+      wait_all_memory();   // the other waves gather (c, s) meanwhile
     }
     PUB_MARK(12);
     PHASE_MARK(3);
@@ -372,9 +371,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       if (wave < 4) {   // the shared row (weights already here) while the routed loads fly
         const int r = w * 4 + wave;
         for (int t = 0; t < n; ++t)
-          emit(t * HW + TOPK * I + r, gateup_row_token(p1_code[wave][0][lane], p1_scale[wave][0][lane >> 2],
-                                                       p1_code[wave][1][lane], p1_scale[wave][1][lane >> 2], a_lds[t],
-                                                       asum_lds[t][lane]));
+          emit(t * HW + TOPK * I + r,
+               gateup_row_token(p1_code[l & 1][0][wave][lane], p1_scale[l & 1][0][wave * (H / G) + (lane >> 2)],
+                                p1_code[l & 1][1][wave][lane], p1_scale[l & 1][1][wave * (H / G) + (lane >> 2)],
+                                a_lds[t], asum_lds[t][lane]));
       }
       compute_batch(j0);
       for (j0 += TB * NWAVES; j0 < 4 + R; j0 += TB * NWAVES) {
@@ -390,13 +390,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         const int word = hloc_idx[k];
         if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      // the next layer's P1 weights: this layer's were last read by the
-      // shared rows above; the other waves gather h meanwhile
-      if (l + 1 < A.l1) {
-        P1Stage q;
-        p1_issue(layer_at(A.base, A.layer_stride, l + 1), q);
-        p1_write(q);
       }
     }
     PUB_MARK(14);
