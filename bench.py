@@ -50,17 +50,84 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack47_traffic.txt")
+DECODE_KERNEL = "k_decode_persistent"
+
+
 def traffic_from_profiles():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", "decode_stack47_traffic.json")
-    if not os.path.exists(p):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(p) as f:
-        d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return int(vals["hbm_bytes_per_launch"])
+
+
+def _counter_values(run_dir, counter, name_pattern=None):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc csv output,
+    keyed by kernel name (optionally only names containing name_pattern)."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                if name_pattern and name_pattern not in name:
+                    continue
+                out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """Write the traffic summary from four rocprofv3 --pmc runs: the decode
+    benchmark (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) and a plain 1 GiB
+    device copy (the same two counters) that calibrates them."""
+    def one(d, counter, pattern):
+        vals = _counter_values(d, counter, pattern)
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {pattern or 'any kernel'} under {d}")
+        name = max(vals, key=lambda k: len(vals[k]))
+        return name, vals[name]
+    copy_bytes = 1 << 30
+    kname, f = one(fetch_dir, "FETCH_SIZE", DECODE_KERNEL)
+    _, w = one(write_dir, "WRITE_SIZE", DECODE_KERNEL)
+    cf = max(max(v) for v in _counter_values(copy_fetch_dir, "FETCH_SIZE").values())
+    cw_all = _counter_values(copy_write_dir, "WRITE_SIZE")
+    cw = max(max(v) for v in cw_all.values())
+    f_factor = copy_bytes / (cf * 1024.0)
+    w_factor = copy_bytes / (cw * 1024.0)
+    f_kib, w_kib = float(np.median(f)), float(np.median(w))
+    total = f_kib * 1024.0 * f_factor + w_kib * 1024.0 * w_factor
+    lines = [
+        "# HBM traffic of one decode launch (47-layer Flint MoE stack, batch 1, the bench workload)",
+        "# from rocprofv3 --pmc, one counter per run, calibrated with a plain 1 GiB device copy",
+        f"kernel: {kname}",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"dispatches_fetch: {len(f)}",
+        f"fetch_kib_per_dispatch_median: {f_kib:.1f}",
+        f"write_kib_per_dispatch_median: {w_kib:.1f}",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_factor: {f_factor:.4f}",
+        f"write_factor: {w_factor:.4f}",
+        f"hbm_bytes_per_launch: {int(round(total))}",
+        f"algorithmic_bytes_per_launch: {TOKEN_BYTES}",
+        f"traffic_over_algorithmic: {total / TOKEN_BYTES:.3f}",
+    ] + [f"command: {c}" for c in commands]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(seconds_budget=20.0):
@@ -104,7 +171,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the traffic summary under profiles/ from four rocprofv3 --pmc output folders")
+    ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
     args = ap.parse_args()
+    if args.counters_summary:
+        summarize_counters(*args.counters_summary, commands=args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the per-GPU shard is the whole block, see the sharding note of the design", file=sys.stderr)

@@ -1,5 +1,6 @@
-"""Helpers for GPU-vs-oracle parity: selection rule, error measures, and
-building a library handle from seeded synthetic layers."""
+"""Helpers for GPU-vs-oracle parity: selection rule, error measures,
+building a library handle from seeded synthetic layers, running a forward
+call and checking one layer teacher-forced against the oracle."""
 import numpy as np
 
 import flintgen as fg
@@ -40,3 +41,36 @@ def rel_l2(got, want):
 def build_layers(synth: fg.Synth, layers, device="cuda"):
     """Generate the given layers on ``device`` (canonical layout tensors)."""
     return [synth.layer(l, device) for l in layers]
+
+
+def run_forward(m, x_np, l0, l1):
+    """forward() on a host array; returns the host result after checking the
+    device error word."""
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
+    out = m.forward(x, l0, l1)
+    torch.cuda.synchronize()
+    m.status()
+    return out.cpu().numpy()
+
+
+def check_layer(src, shape, layer, x_in, x_out, gpu_ids, gpu_w, tight=True):
+    """Teacher-forced check of one token through one layer: the oracle takes
+    the GPU's input residual.  Returns (rel-L2 error, oracle result)."""
+    from oracle import flint_oracle as O
+    a = O.block_input(x_in, shape)
+    res = O.moe_block(a, src, layer, shape)
+    gpu_ids = [int(e) for e in gpu_ids]
+    assert selection_ok(gpu_ids, res.route, shape.top_k), (layer, gpu_ids, res.route.ids, res.route.margin)
+    if gpu_ids != res.route.ids.tolist():
+        # a near tie or an exact-score tie ordered differently: continue with the GPU's set
+        res = O.moe_block(a, src, layer, shape, forced=gpu_ids)
+    np.testing.assert_allclose(gpu_w, res.route.weights, rtol=2e-6, atol=0)
+    x_ref = (x_in.astype(np.float64) + res.delta).astype(np.float32)
+    d_gpu = x_out.astype(np.float64) - x_in.astype(np.float64)
+    d_ref = x_ref.astype(np.float64) - x_in.astype(np.float64)
+    err = rel_l2(d_gpu, d_ref)
+    assert err <= REL_L2_SPEC, (layer, err)
+    if tight:
+        assert err <= REL_L2_DECODE, (layer, err)
+    return err, res

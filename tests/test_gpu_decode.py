@@ -12,9 +12,9 @@ import torch
 
 import flintgen as fg
 import int4_expert_ffn_amd as F
-from oracle import flint_oracle as O
 from oracle_sources import SynthSource
-from parity_util import REL_L2_DECODE, REL_L2_SPEC, build_layers, rel_l2, selection_ok
+from parity_util import build_layers, run_forward
+from parity_util import check_layer as _check_layer
 
 pytestmark = pytest.mark.gpu
 FL = fg.FLINT
@@ -37,32 +37,11 @@ def model():
 
 
 def run(m, x_np, l0, l1):
-    x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
-    out = m.forward(x, l0, l1)
-    torch.cuda.synchronize()
-    m.status()
-    return out.cpu().numpy()
+    return run_forward(m, x_np, l0, l1)
 
 
 def check_layer(synth, layer, x_in, x_out, gpu_ids, gpu_w, tight=True):
-    """Teacher-forced check of one token through one layer."""
-    src = SynthSource(synth)
-    a = O.block_input(x_in, FL)
-    res = O.moe_block(a, src, layer, FL)
-    gpu_ids = [int(e) for e in gpu_ids]
-    assert selection_ok(gpu_ids, res.route, FL.top_k), (layer, gpu_ids, res.route.ids, res.route.margin)
-    if gpu_ids != res.route.ids.tolist():
-        # a near tie or an exact-score tie ordered differently: continue with the GPU's set
-        res = O.moe_block(a, src, layer, FL, forced=gpu_ids)
-    np.testing.assert_allclose(gpu_w, res.route.weights, rtol=2e-6, atol=0)
-    x_ref = (x_in.astype(np.float64) + res.delta).astype(np.float32)
-    d_gpu = x_out.astype(np.float64) - x_in.astype(np.float64)
-    d_ref = x_ref.astype(np.float64) - x_in.astype(np.float64)
-    err = rel_l2(d_gpu, d_ref)
-    assert err <= REL_L2_SPEC, (layer, err)
-    if tight:
-        assert err <= REL_L2_DECODE, (layer, err)
-    return err, res
+    return _check_layer(SynthSource(synth), FL, layer, x_in, x_out, gpu_ids, gpu_w, tight)
 
 
 def test_one_layer_parity(model):
