@@ -97,8 +97,13 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
  * 0 <= layer_begin < layer_end <= n_layers.  Asynchronous on `stream` (a
  * hipStream_t; NULL = the default stream).  One handle serves one stream at a
  * time: calls on a handle must not overlap.  For n_tokens <= 16 each token's
- * result is bitwise independent of n_tokens; larger calls take the prefill
- * path (grouped MFMA GEMM), whose rounding differs (bf16 intermediates). */
+ * result is bitwise independent of n_tokens (decode path).  Larger calls take
+ * the prefill path: tokens sorted by expert, grouped GEMMs on the matrix
+ * cores, the SwiGLU output kept as two bf16 parts (about 16 significant bits)
+ * for the down projection; deterministic, but not bitwise equal to the decode
+ * path.  Each token is still routed and combined independently
+ * (How to Run Flint Locally, "What vLLM changed": prefill runs the same
+ * block over many tokens). */
 int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_begin,
                       int layer_end, float* out, void* stream);
 

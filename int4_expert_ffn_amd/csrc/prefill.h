@@ -1,18 +1,41 @@
-// Prefill path (n_tokens > DECODE_MAX_TOKENS): token->expert sort and grouped
-// MFMA GEMMs.  Interfaces between the runtime and the prefill kernels.
+// Prefill path (DECODE_MAX_TOKENS < n_tokens <= FLINT_MAX_TOKENS): per layer,
+// the block input of every token, a router GEMM, top-6 per token, a
+// deterministic token -> expert sort, and MFMA grouped GEMMs for the routed
+// experts plus dense GEMMs for the shared expert, with a fixed-order combine.
 #pragma once
 #include "decode.h"
 
 namespace flint {
 
+constexpr int PF_TM = 64;                                   // tokens per GEMM tile (two 32-row MFMA blocks)
+constexpr int PF_BW = FLINT_MAX_TOKENS / 32;                // bitmap words per expert
+constexpr int PF_MAX_TILES = (FLINT_MAX_TOKENS * TOPK + PF_TM - 1) / PF_TM + E;
+
+// Device workspace, sized for FLINT_MAX_TOKENS tokens.
 struct PrefillWS {
-  char* base;
+  uint16_t* a;         // [n][H] block input, bf16, 8-element chunks in pair order
+  float* z;            // [n][E] router logits
+  int* ids;            // [n][TOPK] picks (decreasing score)
+  float* w;            // [n][TOPK] routing weights
+  uint32_t* bitmap;    // [E][PF_BW] bit t: token t picked expert e
+  int* offsets;        // [E + 1] first position of expert e's (token, slot) pairs
+  int4* tiles;         // [PF_MAX_TILES] (expert, first position, rows, 0)
+  int* tile_count;     // [1]
+  int* perm;           // [n * TOPK] pair t * TOPK + slot at each position (by expert, then token)
+  uint16_t* h_hi;      // [n * TOPK][I] routed SwiGLU output by position: bf16 high part
+  uint16_t* h_lo;      // [n * TOPK][I] bf16 of the remainder (h - hi); pair-order chunks
+  float* y;            // [n * TOPK][H] routed down output by pair t * TOPK + slot
+  uint16_t* hs_hi;     // [n][IS] shared SwiGLU output, high part
+  uint16_t* hs_lo;     // [n][IS] remainder
 };
 
 typedef int (*alloc_fn)(void** p, size_t bytes, const char* what);
 
+// Allocates the workspace in one block (*mem owns it).
 int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc);
 
+// One layer for n tokens: out = x + moe(rmsnorm(x)).  out may equal xin.
+// trace_ids / trace_w (may be null) receive the picks and weights [n][TOPK].
 hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const PrefillWS& ws,
                                 int* trace_ids, float* trace_w, hipStream_t s);
 

@@ -1,17 +1,542 @@
-// Prefill path: not built yet; forward() reports FLINT_ERR_UNSUPPORTED.
+// Prefill path: a block of n tokens (DECODE_MAX_TOKENS < n <= FLINT_MAX_TOKENS)
+// through one layer, where the block becomes a dense contraction: ~48 tokens
+// per expert on average at n = 2048, so each expert's weights are read once
+// per 64-token tile and multiplied on the matrix cores.
+//
+//   k_pf_input    block input a = bf16(rmsnorm(x)) per token (the decode's
+//                 rounding rule), 8-element chunks in pair order
+//   k_pf_router   z = a Wr^T, bf16 MFMA with fp32 accumulation
+//   k_pf_route    per token (one wave): s = sigmoid(z), c = s + b in fp64,
+//                 top-6 and weights; marks the token in each pick's bitmap
+//   k_pf_offsets  per-expert counts, their exclusive scan, the 64-token tiles
+//   k_pf_scatter  (token, slot) pairs in expert order, tokens increasing
+//                 within an expert (popcounts of the bitmap prefix)
+//   k_pf_gateup   routed gate/up + SwiGLU per tile (grouped GEMM)
+//   k_pf_sh_gateup  shared gate/up + SwiGLU (dense GEMM)
+//   k_pf_down     routed down projection per tile -> y by (token, slot)
+//   k_pf_sh_down  shared down projection and the fixed-order combine
+//                 out = x + ((w0 y0 + w1 y1) + ... + w5 y5) + y_shared
+//
+// Numerics: int4 codes enter the MFMA as bf16 128 + n' (n' = code + 8, exact)
+// against bf16 activations, fp32 accumulation; each 128-element K-group starts
+// from -136 * (sum of the activations over the group), so it holds
+// sum code * a, and is then added to the result times the row's scale.  The
+// SwiGLU output h is kept as two bf16 parts (hi + lo, about 16 significant
+// bits) for the down projection.  Nothing depends on the order of atomic
+// operations, so results are deterministic.
 #include "prefill.h"
+#include "decode_common.h"
 
 namespace flint {
 
-int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn) {
-  ws->base = nullptr;
-  *mem = nullptr;
+constexpr int PF_NT = 256;   // threads of the prefill kernels (4 waves)
+
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf_f32x16 __attribute__((ext_vector_type(16)));
+
+// D = A B + C for 32 x 16 (A) by 16 x 32 (B).  Lane l holds row l % 32 of A
+// and column l % 32 of B, each for k = 8 (l / 32) .. + 7; D register r of lane
+// l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+__device__ __forceinline__ pf_f32x16 mfma_bf16(uint4 a, uint4 b, pf_f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(pf_bf16x8, a), __builtin_bit_cast(pf_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// 8 int4 codes of one dword (k0 in bits 0-3) -> bf16 128 + n' in pair order
+// (k0, k2, k4, k6, k1, k3, k5, k7), n' = code + 8.
+__device__ __forceinline__ uint4 expand_codes(uint32_t code) {
+  const uint32_t x = code ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const uint32_t K43 = 0x43434343u;
+  return make_uint4(__builtin_amdgcn_perm(K43, lo, 0x04010400u), __builtin_amdgcn_perm(K43, lo, 0x04030402u),
+                    __builtin_amdgcn_perm(K43, hi, 0x04010400u), __builtin_amdgcn_perm(K43, hi, 0x04030402u));
+}
+
+// 8 bf16 in natural order (4 dwords) -> pair order
+__device__ __forceinline__ uint4 to_pair_order(uint4 v) {
+  return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                    __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+}
+
+__device__ __forceinline__ float bf16x8_sum(uint4 v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += bf16_bits_to_f32(d[i] & 0xFFFFu) + bf16_bits_to_f32(d[i] >> 16);
+  return s;
+}
+
+// ------------------------------------------------------------- block input
+__global__ void __launch_bounds__(PF_NT) k_pf_input(const float* __restrict__ x, int n, uint16_t* __restrict__ a,
+                                                     uint32_t* __restrict__ bitmap) {
+  __shared__ double red[PF_NT / 64];
+  const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = t * PF_NT + tid; i < E * PF_BW; i += gridDim.x * PF_NT) bitmap[i] = 0u;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)t * H) + 2 * tid;
+  const float4 v0 = xr[0], v1 = xr[1];
+  const double xs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss += xs[j] * xs[j];
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  wg_sync();
+  const double tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const double ms = tot / (double)H + RMS_EPS;
+  const double rinv = rsqrt(ms);
+  double q[8];
+  float qf[8];
+  bool hard = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    q[j] = xs[j] * rinv;
+    qf[j] = (float)q[j];
+    hard |= f32_on_bf16_midpoint(qf[j]);
+  }
+  uint32_t b[8];
+  if (__builtin_expect(__ballot(hard) != 0ull, 0)) {   // wave-uniform, rare: the exact rule
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      double qq = q[j];
+      if (near_bf16_midpoint(qq)) qq = xs[j] / sqrt(ms);
+      b[j] = f64_to_bf16_rne(qq);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = f32_to_bf16_rne(qf[j]);
+  }
+  reinterpret_cast<uint4*>(a + (size_t)t * H)[tid] =
+      make_uint4(b[0] | (b[2] << 16), b[4] | (b[6] << 16), b[1] | (b[3] << 16), b[5] | (b[7] << 16));
+}
+
+// ------------------------------------------------------------- router GEMM
+// 32 tokens x 128 experts per workgroup, 32 experts per wave, K = 2048.
+__global__ void __launch_bounds__(PF_NT) k_pf_router(const uint16_t* __restrict__ a, int n,
+                                                      const uint16_t* __restrict__ router, float* __restrict__ z) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lrow = lane & 31, hl = lane >> 5;
+  const int m0 = blockIdx.x * 32, e = blockIdx.y * 128 + wave * 32 + lrow;
+  const int m = min(m0 + lrow, n - 1);   // rows past n repeat the last token and are not stored
+  const uint4* ar = reinterpret_cast<const uint4*>(a + (size_t)m * H);
+  const uint4* wr = reinterpret_cast<const uint4*>(router + (size_t)e * H);
+  pf_f32x16 acc = {};
+#pragma unroll 8
+  for (int j = 0; j < H / 16; ++j) {
+    const int c = 2 * j + hl;   // 8-element chunk of this lane in MFMA step j
+    acc = mfma_bf16(ar[c], to_pair_order(wr[c]), acc);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int mm = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (mm < n) z[(size_t)mm * E + e] = acc[r];
+  }
+}
+
+// ------------------------------------------------------------- routing
+__global__ void __launch_bounds__(PF_NT) k_pf_route(const float* __restrict__ z, int n, const float* __restrict__ bias,
+                                                     int* __restrict__ ids, float* __restrict__ w,
+                                                     uint32_t* __restrict__ bitmap, int* trace_ids, float* trace_w) {
+  __shared__ double cs[PF_NT / 64][2 * E];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (PF_NT / 64) + wave;
+  if (t >= n) return;   // the whole wave; nothing below waits for other waves
+  double* c = cs[wave];
+#pragma unroll
+  for (int j = 0; j < E / 64; ++j) {
+    const int e = lane + 64 * j;
+    const double s = sigmoid_f64((double)z[(size_t)t * E + e]);
+    double cv = s + (double)bias[e];
+    if (cv != cv) cv = -INFINITY;
+    c[e] = cv;
+    c[E + e] = s;
+  }
+  route_token(c, c + E, ids + (size_t)t * TOPK, w + (size_t)t * TOPK);
+  if (lane < TOPK) {
+    const int id = ids[(size_t)t * TOPK + lane];   // written by this lane above
+    atomicOr(&bitmap[id * PF_BW + (t >> 5)], 1u << (t & 31));
+    if (trace_ids) {
+      trace_ids[(size_t)t * TOPK + lane] = id;
+      trace_w[(size_t)t * TOPK + lane] = w[(size_t)t * TOPK + lane];
+    }
+  }
+}
+
+// ------------------------------------------------------------- sort
+// One workgroup, thread e = expert.
+__global__ void __launch_bounds__(E) k_pf_offsets(const uint32_t* __restrict__ bitmap, int n, int* __restrict__ offsets,
+                                                   int4* __restrict__ tiles, int* __restrict__ tile_count) {
+  __shared__ int sc[2][E], st[2][E];
+  const int e = threadIdx.x;
+  const int nw = (n + 31) >> 5;
+  int cnt = 0;
+  for (int i = 0; i < nw; ++i) cnt += __popc(bitmap[e * PF_BW + i]);
+  const int nt = (cnt + PF_TM - 1) / PF_TM;
+  int vc = cnt, vt = nt, b = 0;
+  for (int d = 1; d < E; d <<= 1) {   // inclusive scans (fixed shape)
+    sc[b][e] = vc;
+    st[b][e] = vt;
+    wg_sync();
+    if (e >= d) {
+      vc += sc[b][e - d];
+      vt += st[b][e - d];
+    }
+    b ^= 1;
+  }
+  const int oc = vc - cnt, ot = vt - nt;
+  offsets[e] = oc;
+  if (e == E - 1) {
+    offsets[E] = vc;
+    *tile_count = vt;
+  }
+  for (int i = 0; i < nt; ++i) tiles[ot + i] = make_int4(e, oc + i * PF_TM, min(PF_TM, cnt - i * PF_TM), 0);
+}
+
+__global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ ids, int n,
+                                                       const uint32_t* __restrict__ bitmap,
+                                                       const int* __restrict__ offsets, int* __restrict__ perm) {
+  const int p = blockIdx.x * PF_NT + threadIdx.x;
+  if (p >= n * TOPK) return;
+  const int t = p / TOPK, e = ids[p];
+  const uint32_t* bm = bitmap + e * PF_BW;
+  int pos = offsets[e];
+  for (int i = 0; i < (t >> 5); ++i) pos += __popc(bm[i]);
+  pos += __popc(bm[t >> 5] & ((1u << (t & 31)) - 1u));
+  perm[pos] = p;
+}
+
+// ------------------------------------------------------------- GEMM tile
+// One workgroup computes 64 tile rows (A rows rows_lds[m], -1 = zero) against
+// 4 waves x NB x 32 weight rows starting at wrow0 (this wave's), for NMAT
+// weight matrices that share A.  A: bf16 rows of lda elements in pair-order
+// chunks, NSPLIT parts whose sum is the operand.  W: int4 codes [rows][KG x 64
+// bytes], S: bf16 scales [rows][KG].  acc[mat][nb][mb] gets row block mb
+// (tile rows 32 mb ..), columns nb x 32 + lane % 32.
+// LDS: a_lds [2][NSPLIT][2][16][32] uint4, nrs_lds [2][2][32].
+template <int NB, int NMAT, int KG, int NSPLIT>
+__device__ __forceinline__ void gemm_tile(const uint16_t* const (&A)[NSPLIT], int lda, const int* rows_lds,
+                                          const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT],
+                                          int wrow0, pf_f32x16 (&acc)[NMAT][NB][2], uint4* a_lds, float* nrs_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
+  const int srow = tid >> 3, scp = tid & 7;   // staging: row, chunk pair
+  constexpr int KB = KG * 64;                 // code bytes per weight row
+
+  // codes and scale bits of this lane's weight rows for one K-group
+  struct Codes {
+    uint4 c[NMAT][NB][2];
+    uint32_t s[NMAT][NB];
+  };
+  auto load_codes = [&](int g, Codes& d) {
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const size_t wr = (size_t)(wrow0 + nb * 32 + lrow);
+        const uint4* p = reinterpret_cast<const uint4*>(W[mat] + wr * KB + g * 64 + hl * 32);
+        d.c[mat][nb][0] = p[0];
+        d.c[mat][nb][1] = p[1];
+        d.s[mat][nb] = S[mat][wr * KG + g];
+      }
+  };
+  uint4 stg[NSPLIT][2][2];
+  auto stage_load = [&](int g) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r = rows_lds[mb * 32 + srow];
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) {
+        if (r >= 0) {
+          const uint4* p = reinterpret_cast<const uint4*>(A[sp] + (size_t)r * lda + g * 128) + 2 * scp;
+          stg[sp][mb][0] = p[0];
+          stg[sp][mb][1] = p[1];
+        } else {
+          stg[sp][mb][0] = make_uint4(0, 0, 0, 0);
+          stg[sp][mb][1] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float part = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp) {
+        uint4* d = a_lds + ((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16) * 32;
+        d[(2 * scp) * 32 + srow] = stg[sp][mb][0];
+        d[(2 * scp + 1) * 32 + srow] = stg[sp][mb][1];
+        part += bf16x8_sum(stg[sp][mb][0]) + bf16x8_sum(stg[sp][mb][1]);
+      }
+      part += dpp_f32<DPP_XOR1>(part);   // the 8 threads of one row
+      part += dpp_f32<DPP_XOR2>(part);
+      part += dpp_f32<DPP_HALF_MIRROR>(part);
+      if (scp == 0) nrs_lds[(buf * 2 + mb) * 32 + srow] = -136.f * part;
+    }
+  };
+
+  // codes run two groups ahead of the MFMAs, the A tile one group ahead
+  Codes c0, c1, c2;
+  load_codes(0, c0);
+  if (KG > 1) load_codes(1, c1);
+  stage_load(0);
+  stage_store(0);
+  wg_sync();
+#pragma unroll 1
+  for (int g = 0; g < KG; ++g) {
+    const int buf = g & 1;
+    if (g + 2 < KG) load_codes(g + 2, c2);
+    if (g + 1 < KG) stage_load(g + 1);
+    pf_f32x16 temp[NMAT][NB][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      pf_f32x16 ci;
+      const float4* nr = reinterpret_cast<const float4*>(nrs_lds + (buf * 2 + mb) * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = nr[2 * q + hl];   // rows 8 q + 4 hl .. + 3
+        ci[4 * q] = v.x;
+        ci[4 * q + 1] = v.y;
+        ci[4 * q + 2] = v.z;
+        ci[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) temp[mat][nb][mb] = ci;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * hl + j;   // chunk of the group
+      uint4 af[NSPLIT][2];
+#pragma unroll
+      for (int sp = 0; sp < NSPLIT; ++sp)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) af[sp][mb] = a_lds[((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16 + c) * 32 + lrow];
+#pragma unroll
+      for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint4 cw = c0.c[mat][nb][j >> 2];
+          const uint32_t dw = (j & 3) == 0 ? cw.x : (j & 3) == 1 ? cw.y : (j & 3) == 2 ? cw.z : cw.w;
+          const uint4 bx = expand_codes(dw);
+#pragma unroll
+          for (int sp = 0; sp < NSPLIT; ++sp)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) temp[mat][nb][mb] = mfma_bf16(af[sp][mb], bx, temp[mat][nb][mb]);
+        }
+    }
+#pragma unroll
+    for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float s = bf16_bits_to_f32(c0.s[mat][nb]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(s, temp[mat][nb][mb][r], acc[mat][nb][mb][r]);
+      }
+    if (g + 1 < KG) stage_store(buf ^ 1);
+    wg_sync();
+    c0 = c1;
+    c1 = c2;
+  }
+}
+
+// tile row of accumulator register r of row block mb
+__device__ __forceinline__ int tile_row(int mb, int r) {
+  return mb * 32 + 8 * (r >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (r & 3);
+}
+
+// h = silu(g) u as bf16 hi + lo at pair-order position of feature col
+__device__ __forceinline__ void store_h(uint16_t* hi_row, uint16_t* lo_row, int col, float g, float u) {
+  const float hv = silu_mul(g, u);
+  const uint32_t hi = f32_to_bf16_rne(hv);
+  const uint32_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
+  const int p = perm_order(col);
+  hi_row[p] = (uint16_t)hi;
+  lo_row[p] = (uint16_t)lo;
+}
+
+constexpr int LDS_A1 = 2 * 1 * 2 * 16 * 32;   // uint4, NSPLIT = 1
+constexpr int LDS_A2 = 2 * 2 * 2 * 16 * 32;   // uint4, NSPLIT = 2
+
+// ------------------------------------------------------------- routed gate/up
+// grid (tiles, I / 128)
+__global__ void __launch_bounds__(PF_NT) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
+                                                      const int* __restrict__ tile_count, const int* __restrict__ perm,
+                                                      LayerW L, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A1];
+  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ int rows[PF_TM];
+  if ((int)blockIdx.x >= *tile_count) return;   // uniform over the workgroup
+  const int4 tl = tiles[blockIdx.x];
+  const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  if (tid < PF_TM) rows[tid] = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
+  wg_sync();
+  const int wrow0 = blockIdx.y * 128 + wave * 32;
+  const uint8_t* const W[2] = {L.gate + (size_t)e * I * (H / 2), L.up + (size_t)e * I * (H / 2)};
+  const uint16_t* const S[2] = {L.gate_s + (size_t)e * I * (H / G), L.up_s + (size_t)e * I * (H / G)};
+  const uint16_t* const Ap[1] = {a};
+  pf_f32x16 acc[2][1][2] = {};
+  gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, nrs);
+  const int col = wrow0 + lrow;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = tile_row(mb, r);
+      if (m < cnt) store_h(h_hi + (size_t)(pos0 + m) * I, h_lo + (size_t)(pos0 + m) * I, col, acc[0][0][mb][r],
+                           acc[1][0][mb][r]);
+    }
+}
+
+// ------------------------------------------------------------- shared gate/up
+// grid (ceil(n / 64), IS / 128)
+__global__ void __launch_bounds__(PF_NT) k_pf_sh_gateup(const uint16_t* __restrict__ a, int n, LayerW L,
+                                                         uint16_t* __restrict__ hs_hi, uint16_t* __restrict__ hs_lo) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A1];
+  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ int rows[PF_TM];
+  const int m0 = blockIdx.x * PF_TM;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+  wg_sync();
+  const int wrow0 = blockIdx.y * 128 + wave * 32;
+  const uint8_t* const W[2] = {L.sh_gate, L.sh_up};
+  const uint16_t* const S[2] = {L.sh_gate_s, L.sh_up_s};
+  const uint16_t* const Ap[1] = {a};
+  pf_f32x16 acc[2][1][2] = {};
+  gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, nrs);
+  const int col = wrow0 + lrow;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + tile_row(mb, r);
+      if (m < n) store_h(hs_hi + (size_t)m * IS, hs_lo + (size_t)m * IS, col, acc[0][0][mb][r], acc[1][0][mb][r]);
+    }
+}
+
+// ------------------------------------------------------------- routed down
+// grid (tiles, H / 256): y[t * TOPK + slot][row] for the tile's pairs
+__global__ void __launch_bounds__(PF_NT) k_pf_down(const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
+                                                    const int4* __restrict__ tiles, const int* __restrict__ tile_count,
+                                                    const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A2];
+  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ int rows[PF_TM];
+  __shared__ int pairs[PF_TM];
+  if ((int)blockIdx.x >= *tile_count) return;
+  const int4 tl = tiles[blockIdx.x];
+  const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  if (tid < PF_TM) {
+    rows[tid] = tid < cnt ? pos0 + tid : -1;
+    pairs[tid] = tid < cnt ? perm[pos0 + tid] : 0;
+  }
+  wg_sync();
+  const int wrow0 = blockIdx.y * 256 + wave * 64;
+  const uint8_t* const W[1] = {L.down + (size_t)e * H * (I / 2)};
+  const uint16_t* const S[1] = {L.down_s + (size_t)e * H * (I / G)};
+  const uint16_t* const Ap[2] = {h_hi, h_lo};
+  pf_f32x16 acc[1][2][2] = {};
+  gemm_tile<2, 1, I / G, 2>(Ap, I, rows, W, S, wrow0, acc, a_lds, nrs);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int col = wrow0 + nb * 32 + lrow;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tile_row(mb, r);
+        if (m < cnt) y[(size_t)pairs[m] * H + col] = acc[0][nb][mb][r];
+      }
+  }
+}
+
+// ------------------------------------------------------------- shared down + combine
+// grid (ceil(n / 64), H / 256)
+__global__ void __launch_bounds__(PF_NT) k_pf_sh_down(const float* xin, float* out, int n,
+                                                       const uint16_t* __restrict__ hs_hi,
+                                                       const uint16_t* __restrict__ hs_lo, LayerW L,
+                                                       const float* __restrict__ w, const float* __restrict__ y) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A2];
+  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ int rows[PF_TM];
+  const int m0 = blockIdx.x * PF_TM;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+  wg_sync();
+  const int wrow0 = blockIdx.y * 256 + wave * 64;
+  const uint8_t* const W[1] = {L.sh_down};
+  const uint16_t* const S[1] = {L.sh_down_s};
+  const uint16_t* const Ap[2] = {hs_hi, hs_lo};
+  pf_f32x16 acc[1][2][2] = {};
+  gemm_tile<2, 1, IS / G, 2>(Ap, IS, rows, W, S, wrow0, acc, a_lds, nrs);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int col = wrow0 + nb * 32 + lrow;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + tile_row(mb, r);
+        if (t < n) {
+          const float* wt = w + (size_t)t * TOPK;
+          const float* yt = y + (size_t)t * TOPK * H + col;
+          float d = wt[0] * yt[0];
+#pragma unroll
+          for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
+          d += acc[0][nb][mb][r];
+          out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------- host side
+int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc) {
+  const size_t T = FLINT_MAX_TOKENS, P = T * TOPK;
+  const size_t sizes[14] = {T * H * 2,      T * E * 4,  T * TOPK * 4, T * TOPK * 4, (size_t)E * PF_BW * 4,
+                            (size_t)(E + 1) * 4, (size_t)PF_MAX_TILES * 16, 4, P * 4, P * I * 2,
+                            P * I * 2,      P * H * 4,  T * IS * 2,   T * IS * 2};
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  size_t tot = 0;
+  for (size_t s : sizes) tot += up(s);
+  char* p = nullptr;
+  const int rc = alloc((void**)&p, tot, "prefill workspace");
+  if (rc) return rc;
+  *mem = p;
+  void** dst[14] = {(void**)&ws->a,     (void**)&ws->z,       (void**)&ws->ids,   (void**)&ws->w,
+                    (void**)&ws->bitmap, (void**)&ws->offsets, (void**)&ws->tiles, (void**)&ws->tile_count,
+                    (void**)&ws->perm,  (void**)&ws->h_hi,    (void**)&ws->h_lo,  (void**)&ws->y,
+                    (void**)&ws->hs_hi, (void**)&ws->hs_lo};
+  for (int i = 0; i < 14; ++i) {
+    *dst[i] = p;
+    p += up(sizes[i]);
+  }
   return FLINT_OK;
 }
 
-hipError_t launch_prefill_layer(const float*, float*, int, const LayerW&, const PrefillWS&, int*, float*,
-                                hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const PrefillWS& ws,
+                                int* trace_ids, float* trace_w, hipStream_t s) {
+  if (n <= DECODE_MAX_TOKENS || n > FLINT_MAX_TOKENS) return hipErrorInvalidValue;
+  const int tiles_max = (n * TOPK + PF_TM - 1) / PF_TM + E;   // <= PF_MAX_TILES
+  const int mt = (n + PF_TM - 1) / PF_TM;
+  hipLaunchKernelGGL(k_pf_input, dim3(n), dim3(PF_NT), 0, s, xin, n, ws.a, ws.bitmap);
+  hipLaunchKernelGGL(k_pf_router, dim3((n + 31) / 32, E / 128), dim3(PF_NT), 0, s, ws.a, n, L.router, ws.z);
+  hipLaunchKernelGGL(k_pf_route, dim3((n + 3) / 4), dim3(PF_NT), 0, s, ws.z, n, L.bias, ws.ids, ws.w, ws.bitmap,
+                     trace_ids, trace_w);
+  hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_count);
+  hipLaunchKernelGGL(k_pf_scatter, dim3((n * TOPK + PF_NT - 1) / PF_NT), dim3(PF_NT), 0, s, ws.ids, n, ws.bitmap,
+                     ws.offsets, ws.perm);
+  hipLaunchKernelGGL(k_pf_gateup, dim3(tiles_max, I / 128), dim3(PF_NT), 0, s, ws.a, ws.tiles, ws.tile_count, ws.perm,
+                     L, ws.h_hi, ws.h_lo);
+  hipLaunchKernelGGL(k_pf_sh_gateup, dim3(mt, IS / 128), dim3(PF_NT), 0, s, ws.a, n, L, ws.hs_hi, ws.hs_lo);
+  hipLaunchKernelGGL(k_pf_down, dim3(tiles_max, H / 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles,
+                     ws.tile_count, ws.perm, L, ws.y);
+  hipLaunchKernelGGL(k_pf_sh_down, dim3(mt, H / 256), dim3(PF_NT), 0, s, xin, out, n, ws.hs_hi, ws.hs_lo, L, ws.w,
+                     ws.y);
+  return hipGetLastError();
 }
 
 }  // namespace flint
