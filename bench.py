@@ -130,6 +130,70 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     print("\n".join(lines))
 
 
+PEAK_BF16_TFLOPS = 2500.0
+PF_TOKENS = 2048
+
+
+def prefill_flops(n):
+    """Algorithmic flops of one layer for n tokens: router GEMM, routed gate/up
+    and down for the n x 6 (token, expert) pairs, shared gate/up and down."""
+    return {"router": 2 * n * E * H, "routed_gate_up": 2 * 2 * n * K * I * H, "routed_down": 2 * n * K * H * I,
+            "shared_gate_up": 2 * 2 * n * IS * H, "shared_down": 2 * n * H * IS}
+
+
+def bench_prefill(args):
+    """One real-shape layer, 2,048 tokens, Zipf-skewed router bias."""
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    synth = fg.Synth(fg.FLINT, seed=0, n_layers=1, bias_kind="zipf")
+    model = F.FlintMoE([synth.layer(0, "cuda")])
+    torch.cuda.empty_cache()
+    n = PF_TOKENS
+    ids = torch.full((1, n, K), -1, dtype=torch.int32, device="cuda")
+    wts = torch.zeros((1, n, K), dtype=torch.float32, device="cuda")
+    model.set_trace(ids, wts, n)
+    x = torch.from_numpy(fg.tokens(0, range(2000, 2000 + n))).cuda()
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        F.flint_moe_forward(model.h, x, n, 0, 1, out, stream)
+    torch.cuda.synchronize()
+    model.status()
+    used = int((torch.bincount(ids[0].flatten().long(), minlength=E) > 0).sum().item())
+    model.set_trace(None, None, 0)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        F.flint_moe_forward(model.h, x, n, 0, 1, out, stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    model.status()
+    durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    layer_s = float(np.median(durs))
+    flops = prefill_flops(n)
+    total = sum(flops.values())
+    weight_bytes = ROUTER_BYTES + used * EXPERT_BYTES + SHARED_BYTES
+    act_bytes = 2 * n * H * 4
+    res = {
+        "metric": "MoE-block prefill tokens/s (one layer, 2048-token chunk)",
+        "value": round(n / layer_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4xbf16->fp32 (MFMA bf16)",
+        "data": "synthetic (seeded int4 weights, bf16 scales, Zipf-skewed router bias, N(0,1) tokens)",
+        "config": {"workload": "one Flint MoE layer, 2048-token prefill chunk", "tokens": n, "experts_used": used,
+                   "algorithmic_flops": total, "flops_by_part": flops},
+        "roofline": {"bound": "mfma", "achieved": round(total / layer_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(total / layer_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "whole layer (9 launches)",
+                     "layer_us_median": round(layer_s * 1e6, 2),
+                     "weight_and_activation_gbps": round((weight_bytes + act_bytes) / layer_s / 1e9, 1)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def cpu_baseline(seconds_budget=20.0):
     """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
     many of the 47 layers as fit the budget; scaled to tokens/s for the whole
@@ -174,9 +238,14 @@ def main():
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the traffic summary under profiles/ from four rocprofv3 --pmc output folders")
     ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the prefill path instead: one layer, a 2048-token chunk")
     args = ap.parse_args()
     if args.counters_summary:
         summarize_counters(*args.counters_summary, commands=args.command)
+        return
+    if args.prefill:
+        bench_prefill(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
