@@ -24,6 +24,8 @@
 // SwiGLU output h is kept as two bf16 parts (hi + lo, about 16 significant
 // bits) for the down projection.  Nothing depends on the order of atomic
 // operations, so results are deterministic.
+#include <algorithm>
+
 #include "prefill.h"
 #include "decode_common.h"
 
@@ -204,17 +206,25 @@ __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ id
 }
 
 // ------------------------------------------------------------- GEMM tile
-// One workgroup computes 64 tile rows (A rows rows_lds[m], -1 = zero) against
-// 4 waves x NB x 32 weight rows starting at wrow0 (this wave's), for NMAT
-// weight matrices that share A.  A: bf16 rows of lda elements in pair-order
-// chunks, NSPLIT parts whose sum is the operand.  W: int4 codes [rows][KG x 64
-// bytes], S: bf16 scales [rows][KG].  acc[mat][nb][mb] gets row block mb
-// (tile rows 32 mb ..), columns nb x 32 + lane % 32.
-// LDS: a_lds [2][NSPLIT][2][16][32] uint4, nrs_lds [2][2][32].
+// One workgroup computes 64 tile rows (rows of A given by rows_lds[m]; -1 is
+// padding: computed from tile row 0, never stored) against NB x 32 weight rows
+// per wave starting at wrow0, for NMAT weight matrices that share A.
+// A: bf16 rows of lda elements in pair-order 8-element chunks, NSPLIT parts
+// whose sum is the operand.  W: int4 codes [rows][KG x 64 bytes], S: bf16
+// scales [rows][KG].  acc[mat][nb][mb] receives row block mb (tile rows
+// 32 mb ..) for columns nb x 32 + lane % 32 of this wave's rows.
+//
+// Per K-group g the MFMAs accumulate sum_k (code_k + 136) a_k from zero, and
+// that is added to acc times the scale s[n][g].  The remaining
+// -136 sum_g s[n][g] R[m][g] (R: sums of A over each group) is one more MFMA
+// step at the end, with R split into three bf16 parts so its products are
+// exact.
+// LDS: a_lds [2][NSPLIT][2][16][32] uint4 (chunk c of tile row r at row
+// position r ^ (c & 14)), rsum_lds [64][KG] floats.
 template <int NB, int NMAT, int KG, int NSPLIT>
 __device__ __forceinline__ void gemm_tile(const uint16_t* const (&A)[NSPLIT], int lda, const int* rows_lds,
                                           const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT],
-                                          int wrow0, pf_f32x16 (&acc)[NMAT][NB][2], uint4* a_lds, float* nrs_lds) {
+                                          int wrow0, pf_f32x16 (&acc)[NMAT][NB][2], uint4* a_lds, float* rsum_lds) {
   const int tid = threadIdx.x, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
   const int srow = tid >> 3, scp = tid & 7;   // staging: row, chunk pair
   constexpr int KB = KG * 64;                 // code bytes per weight row
@@ -236,72 +246,53 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* const (&A)[NSPLIT], in
         d.s[mat][nb] = S[mat][wr * KG + g];
       }
   };
+  // Loads are issued unconditionally so that the wave's memory counter can
+  // wait for the A tile without waiting for the younger code loads: padding
+  // rows read tile row 0, and the last group is re-read.
   uint4 stg[NSPLIT][2][2];
   auto stage_load = [&](int g) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int r = rows_lds[mb * 32 + srow];
+      const int rr = r < 0 ? rows_lds[0] : r;
 #pragma unroll
       for (int sp = 0; sp < NSPLIT; ++sp) {
-        if (r >= 0) {
-          const uint4* p = reinterpret_cast<const uint4*>(A[sp] + (size_t)r * lda + g * 128) + 2 * scp;
-          stg[sp][mb][0] = p[0];
-          stg[sp][mb][1] = p[1];
-        } else {
-          stg[sp][mb][0] = make_uint4(0, 0, 0, 0);
-          stg[sp][mb][1] = make_uint4(0, 0, 0, 0);
-        }
+        const uint4* p = reinterpret_cast<const uint4*>(A[sp] + (size_t)rr * lda + g * 128) + 2 * scp;
+        stg[sp][mb][0] = p[0];
+        stg[sp][mb][1] = p[1];
       }
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, int g, bool sums) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       float part = 0.f;
 #pragma unroll
       for (int sp = 0; sp < NSPLIT; ++sp) {
+        const uint4 v0 = stg[sp][mb][0], v1 = stg[sp][mb][1];
         uint4* d = a_lds + ((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16) * 32;
-        d[(2 * scp) * 32 + srow] = stg[sp][mb][0];
-        d[(2 * scp + 1) * 32 + srow] = stg[sp][mb][1];
-        part += bf16x8_sum(stg[sp][mb][0]) + bf16x8_sum(stg[sp][mb][1]);
+        d[(2 * scp) * 32 + (srow ^ (2 * scp))] = v0;   // rows swizzled by chunk pair: the 16
+        d[(2 * scp + 1) * 32 + (srow ^ (2 * scp))] = v1;   // lanes of one store cycle hit 16 bank groups
+        part += bf16x8_sum(v0) + bf16x8_sum(v1);
       }
       part += dpp_f32<DPP_XOR1>(part);   // the 8 threads of one row
       part += dpp_f32<DPP_XOR2>(part);
       part += dpp_f32<DPP_HALF_MIRROR>(part);
-      if (scp == 0) nrs_lds[(buf * 2 + mb) * 32 + srow] = -136.f * part;
+      if (sums && scp == 0) rsum_lds[(mb * 32 + srow) * KG + g] = part;
     }
   };
 
-  // codes run two groups ahead of the MFMAs, the A tile one group ahead
-  Codes c0, c1, c2;
-  load_codes(0, c0);
-  if (KG > 1) load_codes(1, c1);
-  stage_load(0);
-  stage_store(0);
-  wg_sync();
-#pragma unroll 1
-  for (int g = 0; g < KG; ++g) {
+  // One K-group: codes of group g in `cur`; the codes of group g + 2 are
+  // loaded into `nxt2` and the A tile of g + 1 into registers, then stored
+  // to the other LDS buffer after the MFMAs.
+  auto group = [&](int g, Codes& cur, Codes& nxt2) {
     const int buf = g & 1;
-    if (g + 2 < KG) load_codes(g + 2, c2);
-    if (g + 1 < KG) stage_load(g + 1);
+    stage_load(min(g + 1, KG - 1));
+    load_codes(min(g + 2, KG - 1), nxt2);
+    // keep the loads ahead of the MFMAs, and their first uses (the stores of
+    // the next A tile) after them
+    __builtin_amdgcn_sched_barrier(0);
     pf_f32x16 temp[NMAT][NB][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      pf_f32x16 ci;
-      const float4* nr = reinterpret_cast<const float4*>(nrs_lds + (buf * 2 + mb) * 32);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = nr[2 * q + hl];   // rows 8 q + 4 hl .. + 3
-        ci[4 * q] = v.x;
-        ci[4 * q + 1] = v.y;
-        ci[4 * q + 2] = v.z;
-        ci[4 * q + 3] = v.w;
-      }
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) temp[mat][nb][mb] = ci;
-    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = 8 * hl + j;   // chunk of the group
@@ -309,35 +300,102 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* const (&A)[NSPLIT], in
 #pragma unroll
       for (int sp = 0; sp < NSPLIT; ++sp)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) af[sp][mb] = a_lds[((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16 + c) * 32 + lrow];
+        for (int mb = 0; mb < 2; ++mb)
+          af[sp][mb] = a_lds[((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16 + c) * 32 + (lrow ^ (c & 14))];
 #pragma unroll
       for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const uint4 cw = c0.c[mat][nb][j >> 2];
+          const uint4 cw = cur.c[mat][nb][j >> 2];
           const uint32_t dw = (j & 3) == 0 ? cw.x : (j & 3) == 1 ? cw.y : (j & 3) == 2 ? cw.z : cw.w;
           const uint4 bx = expand_codes(dw);
 #pragma unroll
           for (int sp = 0; sp < NSPLIT; ++sp)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) temp[mat][nb][mb] = mfma_bf16(af[sp][mb], bx, temp[mat][nb][mb]);
+            for (int mb = 0; mb < 2; ++mb)
+              temp[mat][nb][mb] = mfma_bf16(af[sp][mb], bx, (j == 0 && sp == 0) ? pf_f32x16{} : temp[mat][nb][mb]);
         }
     }
 #pragma unroll
     for (int mat = 0; mat < NMAT; ++mat)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const float s = bf16_bits_to_f32(c0.s[mat][nb]);
+        const float sc = bf16_bits_to_f32(cur.s[mat][nb]);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(s, temp[mat][nb][mb][r], acc[mat][nb][mb][r]);
+          for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(sc, temp[mat][nb][mb][r], acc[mat][nb][mb][r]);
       }
-    if (g + 1 < KG) stage_store(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store(buf ^ 1, g + 1, g + 1 < KG);   // after the last group: unused
     wg_sync();
+  };
+
+  // Codes run two groups ahead of the MFMAs (three register sets, rotated
+  // after each group), the A tile one group ahead.
+  Codes c0, c1, c2;
+  load_codes(0, c0);
+  load_codes(min(1, KG - 1), c1);
+  stage_load(0);
+  stage_store(0, 0, true);
+  wg_sync();
+#pragma unroll 1
+  for (int g = 0; g < KG; ++g) {
+    group(g, c0, c2);
     c0 = c1;
     c1 = c2;
   }
+
+  // -136 sum_g s[n][g] R[m][g]: K = the KG groups (zero-padded to 16)
+  uint4 rp[3][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    uint32_t h2[4], m2[4], l2[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      float v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int g = 8 * hl + i + u;
+        v[u] = g < KG ? rsum_lds[(mb * 32 + lrow) * KG + g] : 0.f;
+      }
+      uint32_t hb[2], mbits[2], lb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        hb[u] = f32_to_bf16_rne(v[u]);
+        const float r1 = v[u] - bf16_bits_to_f32(hb[u]);
+        mbits[u] = f32_to_bf16_rne(r1);
+        lb[u] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mbits[u]));
+      }
+      h2[i / 2] = hb[0] | (hb[1] << 16);
+      m2[i / 2] = mbits[0] | (mbits[1] << 16);
+      l2[i / 2] = lb[0] | (lb[1] << 16);
+    }
+    rp[0][mb] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+    rp[1][mb] = make_uint4(m2[0], m2[1], m2[2], m2[3]);
+    rp[2][mb] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+  }
+#pragma unroll
+  for (int mat = 0; mat < NMAT; ++mat)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint16_t* sp = S[mat] + (size_t)(wrow0 + nb * 32 + lrow) * KG;
+      uint32_t sw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int g = 8 * hl + i;
+        if (g + 1 < KG) sw[i / 2] = (uint32_t)sp[g] | ((uint32_t)sp[g + 1] << 16);
+      }
+      const uint4 sb = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        pf_f32x16 corr = mfma_bf16(rp[0][mb], sb, pf_f32x16{});
+        corr = mfma_bf16(rp[1][mb], sb, corr);
+        corr = mfma_bf16(rp[2][mb], sb, corr);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(-136.f, corr[r], acc[mat][nb][mb][r]);
+      }
+    }
 }
 
 // tile row of accumulator register r of row block mb
@@ -358,138 +416,174 @@ __device__ __forceinline__ void store_h(uint16_t* hi_row, uint16_t* lo_row, int 
 constexpr int LDS_A1 = 2 * 1 * 2 * 16 * 32;   // uint4, NSPLIT = 1
 constexpr int LDS_A2 = 2 * 2 * 2 * 16 * 32;   // uint4, NSPLIT = 2
 
+// Work items of the persistent GEMM kernels: (tile, N-slice) pairs, numbered
+// so that the NT slices of one tile are 8 apart (one XCD, whose L2 then holds
+// the tile's A rows) and come up in the same round of the grid.
+__device__ __forceinline__ void pf_item(int q, int nt_count, int& tile, int& nt) {
+  tile = 8 * (q / (8 * nt_count)) + (q & 7);
+  nt = (q >> 3) % nt_count;
+}
+__host__ __device__ constexpr int pf_items(int tiles, int nt_count) { return (tiles + 7) / 8 * 8 * nt_count; }
+
 // ------------------------------------------------------------- routed gate/up
-// grid (tiles, I / 128)
-__global__ void __launch_bounds__(PF_NT) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
+__global__ void __launch_bounds__(PF_NT, 2) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
                                                       const int* __restrict__ tile_count, const int* __restrict__ perm,
                                                       LayerW L, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   __shared__ __align__(16) uint4 a_lds[LDS_A1];
-  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ __align__(16) float rsum[PF_TM * (H / G)];
   __shared__ int rows[PF_TM];
-  if ((int)blockIdx.x >= *tile_count) return;   // uniform over the workgroup
-  const int4 tl = tiles[blockIdx.x];
-  const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+  constexpr int NT = I / 128;
+  const int T = *tile_count;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  if (tid < PF_TM) rows[tid] = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
-  wg_sync();
-  const int wrow0 = blockIdx.y * 128 + wave * 32;
-  const uint8_t* const W[2] = {L.gate + (size_t)e * I * (H / 2), L.up + (size_t)e * I * (H / 2)};
-  const uint16_t* const S[2] = {L.gate_s + (size_t)e * I * (H / G), L.up_s + (size_t)e * I * (H / G)};
-  const uint16_t* const Ap[1] = {a};
-  pf_f32x16 acc[2][1][2] = {};
-  gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, nrs);
-  const int col = wrow0 + lrow;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = tile_row(mb, r);
-      if (m < cnt) store_h(h_hi + (size_t)(pos0 + m) * I, h_lo + (size_t)(pos0 + m) * I, col, acc[0][0][mb][r],
-                           acc[1][0][mb][r]);
-    }
-}
-
-// ------------------------------------------------------------- shared gate/up
-// grid (ceil(n / 64), IS / 128)
-__global__ void __launch_bounds__(PF_NT) k_pf_sh_gateup(const uint16_t* __restrict__ a, int n, LayerW L,
-                                                         uint16_t* __restrict__ hs_hi, uint16_t* __restrict__ hs_lo) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A1];
-  __shared__ __align__(16) float nrs[2 * 2 * 32];
-  __shared__ int rows[PF_TM];
-  const int m0 = blockIdx.x * PF_TM;
-  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
-  wg_sync();
-  const int wrow0 = blockIdx.y * 128 + wave * 32;
-  const uint8_t* const W[2] = {L.sh_gate, L.sh_up};
-  const uint16_t* const S[2] = {L.sh_gate_s, L.sh_up_s};
-  const uint16_t* const Ap[1] = {a};
-  pf_f32x16 acc[2][1][2] = {};
-  gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, nrs);
-  const int col = wrow0 + lrow;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + tile_row(mb, r);
-      if (m < n) store_h(hs_hi + (size_t)m * IS, hs_lo + (size_t)m * IS, col, acc[0][0][mb][r], acc[1][0][mb][r]);
-    }
-}
-
-// ------------------------------------------------------------- routed down
-// grid (tiles, H / 256): y[t * TOPK + slot][row] for the tile's pairs
-__global__ void __launch_bounds__(PF_NT) k_pf_down(const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
-                                                    const int4* __restrict__ tiles, const int* __restrict__ tile_count,
-                                                    const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A2];
-  __shared__ __align__(16) float nrs[2 * 2 * 32];
-  __shared__ int rows[PF_TM];
-  __shared__ int pairs[PF_TM];
-  if ((int)blockIdx.x >= *tile_count) return;
-  const int4 tl = tiles[blockIdx.x];
-  const int e = tl.x, pos0 = tl.y, cnt = tl.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  if (tid < PF_TM) {
-    rows[tid] = tid < cnt ? pos0 + tid : -1;
-    pairs[tid] = tid < cnt ? perm[pos0 + tid] : 0;
-  }
-  wg_sync();
-  const int wrow0 = blockIdx.y * 256 + wave * 64;
-  const uint8_t* const W[1] = {L.down + (size_t)e * H * (I / 2)};
-  const uint16_t* const S[1] = {L.down_s + (size_t)e * H * (I / G)};
-  const uint16_t* const Ap[2] = {h_hi, h_lo};
-  pf_f32x16 acc[1][2][2] = {};
-  gemm_tile<2, 1, I / G, 2>(Ap, I, rows, W, S, wrow0, acc, a_lds, nrs);
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int col = wrow0 + nb * 32 + lrow;
+  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
+    int ti, nt;
+    pf_item(q, NT, ti, nt);
+    if (ti >= T) continue;   // uniform over the workgroup
+    const int4 tl = tiles[ti];
+    const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+    wg_sync();   // the previous item is done with the LDS
+    if (tid < PF_TM) rows[tid] = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
+    wg_sync();
+    const int wrow0 = nt * 128 + wave * 32;
+    const uint8_t* const W[2] = {L.gate + (size_t)e * I * (H / 2), L.up + (size_t)e * I * (H / 2)};
+    const uint16_t* const S[2] = {L.gate_s + (size_t)e * I * (H / G), L.up_s + (size_t)e * I * (H / G)};
+    const uint16_t* const Ap[1] = {a};
+    pf_f32x16 acc[2][1][2] = {};
+    gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, rsum);
+    const int col = wrow0 + lrow;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = tile_row(mb, r);
-        if (m < cnt) y[(size_t)pairs[m] * H + col] = acc[0][nb][mb][r];
+        if (m < cnt) store_h(h_hi + (size_t)(pos0 + m) * I, h_lo + (size_t)(pos0 + m) * I, col, acc[0][0][mb][r],
+                             acc[1][0][mb][r]);
       }
   }
 }
 
+// ------------------------------------------------------------- shared gate/up
+__global__ void __launch_bounds__(PF_NT, 2) k_pf_sh_gateup(const uint16_t* __restrict__ a, int n, LayerW L,
+                                                         uint16_t* __restrict__ hs_hi, uint16_t* __restrict__ hs_lo) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A1];
+  __shared__ __align__(16) float rsum[PF_TM * (H / G)];
+  __shared__ int rows[PF_TM];
+  constexpr int NT = IS / 128;
+  const int T = (n + PF_TM - 1) / PF_TM;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
+    int ti, nt;
+    pf_item(q, NT, ti, nt);
+    if (ti >= T) continue;
+    const int m0 = ti * PF_TM;
+    wg_sync();
+    if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+    wg_sync();
+    const int wrow0 = nt * 128 + wave * 32;
+    const uint8_t* const W[2] = {L.sh_gate, L.sh_up};
+    const uint16_t* const S[2] = {L.sh_gate_s, L.sh_up_s};
+    const uint16_t* const Ap[1] = {a};
+    pf_f32x16 acc[2][1][2] = {};
+    gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, rsum);
+    const int col = wrow0 + lrow;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + tile_row(mb, r);
+        if (m < n) store_h(hs_hi + (size_t)m * IS, hs_lo + (size_t)m * IS, col, acc[0][0][mb][r], acc[1][0][mb][r]);
+      }
+  }
+}
+
+// ------------------------------------------------------------- routed down
+// y[t * TOPK + slot][row] for every (token, slot) pair of each tile
+__global__ void __launch_bounds__(PF_NT) k_pf_down(const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
+                                                    const int4* __restrict__ tiles, const int* __restrict__ tile_count,
+                                                    const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
+  __shared__ __align__(16) uint4 a_lds[LDS_A2];
+  __shared__ __align__(16) float rsum[PF_TM * (I / G)];
+  __shared__ int rows[PF_TM];
+  __shared__ int pairs[PF_TM];
+  constexpr int NT = H / 256;
+  const int T = *tile_count;
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
+    int ti, nt;
+    pf_item(q, NT, ti, nt);
+    if (ti >= T) continue;
+    const int4 tl = tiles[ti];
+    const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+    wg_sync();
+    if (tid < PF_TM) {
+      rows[tid] = tid < cnt ? pos0 + tid : -1;
+      pairs[tid] = tid < cnt ? perm[pos0 + tid] : 0;
+    }
+    wg_sync();
+    const int wrow0 = nt * 256 + wave * 64;
+    const uint8_t* const W[1] = {L.down + (size_t)e * H * (I / 2)};
+    const uint16_t* const S[1] = {L.down_s + (size_t)e * H * (I / G)};
+    const uint16_t* const Ap[2] = {h_hi, h_lo};
+    pf_f32x16 acc[1][2][2] = {};
+    gemm_tile<2, 1, I / G, 2>(Ap, I, rows, W, S, wrow0, acc, a_lds, rsum);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = wrow0 + nb * 32 + lrow;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = tile_row(mb, r);
+          if (m < cnt) y[(size_t)pairs[m] * H + col] = acc[0][nb][mb][r];
+        }
+    }
+  }
+}
+
 // ------------------------------------------------------------- shared down + combine
-// grid (ceil(n / 64), H / 256)
 __global__ void __launch_bounds__(PF_NT) k_pf_sh_down(const float* xin, float* out, int n,
                                                        const uint16_t* __restrict__ hs_hi,
                                                        const uint16_t* __restrict__ hs_lo, LayerW L,
                                                        const float* __restrict__ w, const float* __restrict__ y) {
   __shared__ __align__(16) uint4 a_lds[LDS_A2];
-  __shared__ __align__(16) float nrs[2 * 2 * 32];
+  __shared__ __align__(16) float rsum[PF_TM * (IS / G)];
   __shared__ int rows[PF_TM];
-  const int m0 = blockIdx.x * PF_TM;
+  constexpr int NT = H / 256;
+  const int T = (n + PF_TM - 1) / PF_TM;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
-  wg_sync();
-  const int wrow0 = blockIdx.y * 256 + wave * 64;
-  const uint8_t* const W[1] = {L.sh_down};
-  const uint16_t* const S[1] = {L.sh_down_s};
-  const uint16_t* const Ap[2] = {hs_hi, hs_lo};
-  pf_f32x16 acc[1][2][2] = {};
-  gemm_tile<2, 1, IS / G, 2>(Ap, IS, rows, W, S, wrow0, acc, a_lds, nrs);
+  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
+    int ti, nt;
+    pf_item(q, NT, ti, nt);
+    if (ti >= T) continue;
+    const int m0 = ti * PF_TM;
+    wg_sync();
+    if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+    wg_sync();
+    const int wrow0 = nt * 256 + wave * 64;
+    const uint8_t* const W[1] = {L.sh_down};
+    const uint16_t* const S[1] = {L.sh_down_s};
+    const uint16_t* const Ap[2] = {hs_hi, hs_lo};
+    pf_f32x16 acc[1][2][2] = {};
+    gemm_tile<2, 1, IS / G, 2>(Ap, IS, rows, W, S, wrow0, acc, a_lds, rsum);
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int col = wrow0 + nb * 32 + lrow;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = wrow0 + nb * 32 + lrow;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = m0 + tile_row(mb, r);
-        if (t < n) {
-          const float* wt = w + (size_t)t * TOPK;
-          const float* yt = y + (size_t)t * TOPK * H + col;
-          float d = wt[0] * yt[0];
+        for (int r = 0; r < 16; ++r) {
+          const int t = m0 + tile_row(mb, r);
+          if (t < n) {
+            const float* wt = w + (size_t)t * TOPK;
+            const float* yt = y + (size_t)t * TOPK * H + col;
+            float d = wt[0] * yt[0];
 #pragma unroll
-          for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
-          d += acc[0][nb][mb][r];
-          out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
+            for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
+            d += acc[0][nb][mb][r];
+            out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
+          }
         }
-      }
+    }
   }
 }
 
@@ -529,13 +623,16 @@ hipError_t launch_prefill_layer(const float* xin, float* out, int n, const Layer
   hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_count);
   hipLaunchKernelGGL(k_pf_scatter, dim3((n * TOPK + PF_NT - 1) / PF_NT), dim3(PF_NT), 0, s, ws.ids, n, ws.bitmap,
                      ws.offsets, ws.perm);
-  hipLaunchKernelGGL(k_pf_gateup, dim3(tiles_max, I / 128), dim3(PF_NT), 0, s, ws.a, ws.tiles, ws.tile_count, ws.perm,
-                     L, ws.h_hi, ws.h_lo);
-  hipLaunchKernelGGL(k_pf_sh_gateup, dim3(mt, IS / 128), dim3(PF_NT), 0, s, ws.a, n, L, ws.hs_hi, ws.hs_lo);
-  hipLaunchKernelGGL(k_pf_down, dim3(tiles_max, H / 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles,
-                     ws.tile_count, ws.perm, L, ws.y);
-  hipLaunchKernelGGL(k_pf_sh_down, dim3(mt, H / 256), dim3(PF_NT), 0, s, xin, out, n, ws.hs_hi, ws.hs_lo, L, ws.w,
-                     ws.y);
+  // persistent grids: about one round of resident workgroups, at most one per item
+  auto grid = [](int items, int resident) { return dim3(std::max(1, std::min(items, resident))); };
+  hipLaunchKernelGGL(k_pf_gateup, grid(pf_items(tiles_max, I / 128), 2 * 256), dim3(PF_NT), 0, s, ws.a, ws.tiles,
+                     ws.tile_count, ws.perm, L, ws.h_hi, ws.h_lo);
+  hipLaunchKernelGGL(k_pf_sh_gateup, grid(pf_items(mt, IS / 128), 2 * 256), dim3(PF_NT), 0, s, ws.a, n, L, ws.hs_hi,
+                     ws.hs_lo);
+  hipLaunchKernelGGL(k_pf_down, grid(pf_items(tiles_max, H / 256), 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo,
+                     ws.tiles, ws.tile_count, ws.perm, L, ws.y);
+  hipLaunchKernelGGL(k_pf_sh_down, grid(pf_items(mt, H / 256), 256), dim3(PF_NT), 0, s, xin, out, n, ws.hs_hi,
+                     ws.hs_lo, L, ws.w, ws.y);
   return hipGetLastError();
 }
 
