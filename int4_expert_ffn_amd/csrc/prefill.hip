@@ -18,12 +18,14 @@
 //                 out = x + ((w0 y0 + w1 y1) + ... + w5 y5) + y_shared
 //
 // Numerics: int4 codes enter the MFMA as bf16 128 + n' (n' = code + 8, exact)
-// against bf16 activations, fp32 accumulation; each 128-element K-group starts
-// from -136 * (sum of the activations over the group), so it holds
-// sum code * a, and is then added to the result times the row's scale.  The
-// SwiGLU output h is kept as two bf16 parts (hi + lo, about 16 significant
-// bits) for the down projection.  Nothing depends on the order of atomic
-// operations, so results are deterministic.
+// against bf16 activations, fp32 accumulation.  Each 128-element K-group is
+// accumulated from zero, giving sum (code + 136) a, and added to the result
+// times the row's scale; one last MFMA step subtracts 136 sum_g s_g R_g
+// (R_g: sum of the activations over group g, split into three bf16 parts so
+// that the products are exact).  The SwiGLU output h is kept as two bf16
+// parts (hi + lo, about 16 significant bits) for the down projection.
+// Nothing depends on the order of atomic operations, so results are
+// deterministic.
 #include <algorithm>
 
 #include "prefill.h"
