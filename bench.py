@@ -194,6 +194,94 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def build_stack_model(dev):
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    synth = fg.flint_stack(0, N_LAYERS)
+    layers = [synth.layer(l, dev) for l in range(N_LAYERS)]
+    torch.cuda.synchronize()
+    model = F.FlintMoE(layers)
+    del layers
+    torch.cuda.empty_cache()
+    return model
+
+
+COST_TABLE_FILE = os.path.join(ROOT, "profiles", "decode_cost_table_stack47.txt")
+
+
+def bench_cost_table(args):
+    """Verify-block cost table: one forward call of n = 1..16 independent tokens
+    through the 47 layers (the decode path), median time per call.  Algorithmic
+    bytes per call count each layer's router, shared expert and the distinct
+    routed experts the call's tokens picked (from the trace)."""
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    dev = torch.device("cuda:0")
+    model = build_stack_model(dev)
+    cap = 16
+    pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
+    ids = torch.full((N_LAYERS, cap, K), -1, dtype=torch.int32, device=dev)
+    wts = torch.zeros((N_LAYERS, cap, K), dtype=torch.float32, device=dev)
+    out = torch.empty((cap, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    batches = 4                         # distinct token batches per n, used in turn
+    rows = []
+    for n in range(1, cap + 1):
+        xs = [pool[b * 16:b * 16 + n] for b in range(batches)]
+        # distinct experts per layer of each batch, from one traced call
+        model.set_trace(ids, wts, cap)
+        call_bytes = []
+        for x in xs:
+            F.flint_moe_forward(model.h, x, n, 0, N_LAYERS, out, stream)
+            torch.cuda.synchronize()
+            tr = ids[:, :n].cpu().numpy()
+            distinct = [len(np.unique(tr[l])) for l in range(N_LAYERS)]
+            call_bytes.append(sum(ROUTER_BYTES + SHARED_BYTES + d * EXPERT_BYTES for d in distinct))
+        model.set_trace(None, None, 0)
+        for i in range(args.warmup):
+            F.flint_moe_forward(model.h, xs[i % batches], n, 0, N_LAYERS, out, stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            F.flint_moe_forward(model.h, xs[i % batches], n, 0, N_LAYERS, out, stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        model.status()
+        durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        med = float(np.median(durs))
+        mean_bytes = float(np.mean([call_bytes[i % batches] for i in range(args.steps)]))
+        rows.append({"n": n, "us_median": round(med * 1e6, 1),
+                     "us_p10": round(float(np.percentile(durs, 10)) * 1e6, 1),
+                     "us_p90": round(float(np.percentile(durs, 90)) * 1e6, 1),
+                     "tokens_per_s": round(n / med, 1),
+                     "distinct_experts_per_layer": round((mean_bytes / N_LAYERS - ROUTER_BYTES - SHARED_BYTES)
+                                                         / EXPERT_BYTES, 2),
+                     "algorithmic_bytes": int(mean_bytes),
+                     "gbps": round(mean_bytes / med / 1e9, 1)})
+        print(f"n={n}: {rows[-1]}", file=sys.stderr, flush=True)
+    if args.cost_table_out:
+        with open(args.cost_table_out, "w") as f:
+            f.write("# Verify-block cost table: one flint_moe_forward call of n independent tokens through the\n"
+                    "# 47-layer stack (decode path), hip events on the launch stream, "
+                    f"{args.steps} timed calls per n after {args.warmup} warm-up, 4 token batches per n in turn.\n"
+                    "# bytes: router + shared + distinct routed experts per layer (from the trace), summed over layers.\n"
+                    "# command: python bench.py --cost-table --steps "
+                    f"{args.steps} --warmup {args.warmup} --cost-table-out <file>\n")
+            f.write("n,us_median,us_p10,us_p90,tokens_per_s,distinct_experts_per_layer,algorithmic_bytes,gbps,frac_of_8tbs\n")
+            for r in rows:
+                f.write(f"{r['n']},{r['us_median']},{r['us_p10']},{r['us_p90']},{r['tokens_per_s']},"
+                        f"{r['distinct_experts_per_layer']},{r['algorithmic_bytes']},{r['gbps']},"
+                        f"{r['gbps'] / PEAK_HBM_GBPS:.4f}\n")
+    print(json.dumps({"metric": "verify-block cost table (47-layer decode call time for n = 1..16 tokens)",
+                      "unit": "us per call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic (seeded int4 weights, bf16 scales, N(0,1) tokens)",
+                      "config": {"workload": "47-layer Flint MoE block stack, n independent tokens per call"},
+                      "table": rows}), flush=True)
+
+
 def cpu_baseline(seconds_budget=20.0):
     """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
     many of the 47 layers as fit the budget; scaled to tokens/s for the whole
@@ -240,12 +328,18 @@ def main():
     ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill path instead: one layer, a 2048-token chunk")
+    ap.add_argument("--cost-table", action="store_true",
+                    help="time one 47-layer call for n = 1..16 tokens (verify-block cost table)")
+    ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
     args = ap.parse_args()
     if args.counters_summary:
         summarize_counters(*args.counters_summary, commands=args.command)
         return
     if args.prefill:
         bench_prefill(args)
+        return
+    if args.cost_table:
+        bench_cost_table(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -267,14 +361,7 @@ def main():
         return
 
     t_setup = time.perf_counter()
-    synth = fg.flint_stack(0, N_LAYERS)
-    layers = []
-    for l in range(N_LAYERS):
-        layers.append(synth.layer(l, dev))
-    torch.cuda.synchronize()
-    model = F.FlintMoE(layers)
-    del layers
-    torch.cuda.empty_cache()
+    model = build_stack_model(dev)
     pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
     out = torch.empty((1, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()

@@ -72,16 +72,31 @@ def test_stack_composes_and_matches_per_layer(model):
 
 def test_batch_invariance_bitwise(model):
     synth, m, ids, w = model
-    x = fg.tokens(0, range(200, 209))
+    x = fg.tokens(0, range(200, 200 + CAP))
     singles, sids = [], []
-    for t in range(9):
+    for t in range(CAP):
         singles.append(run(m, x[t:t + 1], 0, N_LAYERS)[0])
         sids.append(ids[:, 0].cpu().numpy().copy())
-    for n in (4, 9):
+    for n in (4, 9, CAP):
         out = run(m, x[:n], 0, N_LAYERS)
         for t in range(n):
             assert np.array_equal(out[t], singles[t]), (n, t)
             assert np.array_equal(ids[:, t].cpu().numpy(), sids[t]), (n, t)
+
+
+def test_largest_decode_batch_parity(model):
+    """16 tokens in one call (the largest decode batch, up to 96 distinct
+    experts per layer): every token of every layer against the oracle."""
+    synth, m, ids, w = model
+    x = fg.tokens(0, range(600, 600 + CAP))
+    cur = x
+    for l in range(N_LAYERS):
+        nxt = run(m, cur, l, l + 1)
+        for t in range(CAP):
+            check_layer(synth, l, cur[t], nxt[t], ids[l, t].cpu().numpy(), w[l, t].cpu().numpy())
+        cur = nxt
+    distinct = len(set(ids[0].cpu().numpy().ravel().tolist()))
+    print(f"distinct experts in layer 0: {distinct}")
 
 
 def test_determinism_and_in_place(model):
