@@ -19,8 +19,8 @@ struct PrefillWS {
   float* w;            // [n][TOPK] routing weights
   uint32_t* bitmap;    // [E][PF_BW] bit t: token t picked expert e
   int* offsets;        // [E + 1] first position of expert e's (token, slot) pairs
-  int4* tiles;         // [PF_MAX_TILES] (expert, first position, rows, 0)
-  int* tile_count;     // [1]
+  int4* tiles;         // [PF_MAX_TILES] (expert, first position, rows, 0), grouped by XCD
+  int* tile_start;     // [9] the tiles for XCD x (blockIdx % 8) are [tile_start[x], tile_start[x + 1])
   int* perm;           // [n * TOPK] pair t * TOPK + slot at each position (by expert, then token)
   uint16_t* h_hi;      // [n * TOPK][I] routed SwiGLU output by position: bf16 high part
   uint16_t* h_lo;      // [n * TOPK][I] bf16 of the remainder (h - hi); pair-order chunks

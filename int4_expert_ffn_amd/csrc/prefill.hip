@@ -165,33 +165,72 @@ __global__ void __launch_bounds__(PF_NT) k_pf_route(const float* __restrict__ z,
 }
 
 // ------------------------------------------------------------- sort
-// One workgroup, thread e = expert.
+// One workgroup, thread e = expert.  Besides the offsets, the 64-row tiles are
+// listed grouped by XCD: experts are ranked by tile count (then index) and
+// dealt to the 8 XCDs in snake order (0..7, 7..0, ...), so that all tiles of
+// one expert run on one XCD, whose L2 then holds the expert's weights, and
+// the XCDs get similar amounts of work.  Workgroup b of the GEMM kernels runs
+// on XCD b % 8 (round-robin dispatch); only speed depends on that.
+__device__ __forceinline__ int snake_rank(int x, int j) { return 16 * (j >> 1) + ((j & 1) ? 15 - x : x); }
+
+constexpr int PF_NT_BINS = FLINT_MAX_TOKENS / PF_TM + 1;   // tile counts 0..32 of one expert
+
 __global__ void __launch_bounds__(E) k_pf_offsets(const uint32_t* __restrict__ bitmap, int n, int* __restrict__ offsets,
-                                                   int4* __restrict__ tiles, int* __restrict__ tile_count) {
-  __shared__ int sc[2][E], st[2][E];
+                                                   int4* __restrict__ tiles, int* __restrict__ tile_start) {
+  __shared__ int sc[2][E];
+  __shared__ int nt_hist[PF_NT_BINS];
+  __shared__ uint32_t nt_mask[PF_NT_BINS][E / 32];   // experts with a given tile count
+  __shared__ int nt_by_rank[E], xcd_tiles[8];
   const int e = threadIdx.x;
-  const int nw = (n + 31) >> 5;
+  for (int i = e; i < PF_NT_BINS * (E / 32); i += E) (&nt_mask[0][0])[i] = 0u;
+  if (e < PF_NT_BINS) nt_hist[e] = 0;
+  // the bitmap is cleared in full for every layer, so all words are read
+  const uint4* bm = reinterpret_cast<const uint4*>(bitmap + e * PF_BW);
   int cnt = 0;
-  for (int i = 0; i < nw; ++i) cnt += __popc(bitmap[e * PF_BW + i]);
+#pragma unroll
+  for (int i = 0; i < PF_BW / 4; ++i) {
+    const uint4 v = bm[i];
+    cnt += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+  }
   const int nt = (cnt + PF_TM - 1) / PF_TM;
-  int vc = cnt, vt = nt, b = 0;
-  for (int d = 1; d < E; d <<= 1) {   // inclusive scans (fixed shape)
+  wg_sync();
+  atomicAdd(&nt_hist[nt], 1);
+  atomicOr(&nt_mask[nt][e >> 5], 1u << (e & 31));
+  int vc = cnt, b = 0;
+  for (int d = 1; d < E; d <<= 1) {   // inclusive scan (fixed shape); its barriers also order the atomics
     sc[b][e] = vc;
-    st[b][e] = vt;
     wg_sync();
-    if (e >= d) {
-      vc += sc[b][e - d];
-      vt += st[b][e - d];
-    }
+    if (e >= d) vc += sc[b][e - d];
     b ^= 1;
   }
-  const int oc = vc - cnt, ot = vt - nt;
+  const int oc = vc - cnt;
   offsets[e] = oc;
-  if (e == E - 1) {
-    offsets[E] = vc;
-    *tile_count = vt;
+  if (e == E - 1) offsets[E] = vc;
+  // rank: experts with more tiles first, equal counts by index
+  int r = 0;
+  for (int v = nt + 1; v < PF_NT_BINS; ++v) r += nt_hist[v];
+  for (int w = 0; w < (e >> 5); ++w) r += __popc(nt_mask[nt][w]);
+  r += __popc(nt_mask[nt][e >> 5] & ((1u << (e & 31)) - 1u));
+  nt_by_rank[r] = nt;
+  wg_sync();
+  const int u = r & 15, x = u < 8 ? u : 15 - u, j = r >> 3;
+  int before = 0;   // tiles of the experts dealt to XCD x ahead of this one
+  for (int jj = 0; jj < j; ++jj) before += nt_by_rank[snake_rank(x, jj)];
+  if (e < 8) {
+    int tot = 0;
+    for (int jj = 0; jj < E / 8; ++jj) tot += nt_by_rank[snake_rank(e, jj)];
+    xcd_tiles[e] = tot;
   }
-  for (int i = 0; i < nt; ++i) tiles[ot + i] = make_int4(e, oc + i * PF_TM, min(PF_TM, cnt - i * PF_TM), 0);
+  wg_sync();
+  int base = 0;
+  for (int xx = 0; xx < x; ++xx) base += xcd_tiles[xx];
+  if (e <= 8) {
+    int s0 = 0;
+    for (int xx = 0; xx < e; ++xx) s0 += xcd_tiles[xx];
+    tile_start[e] = s0;
+  }
+  for (int i = 0; i < nt; ++i)
+    tiles[base + before + i] = make_int4(e, oc + i * PF_TM, min(PF_TM, cnt - i * PF_TM), 0);
 }
 
 __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ ids, int n,
@@ -429,19 +468,18 @@ __host__ __device__ constexpr int pf_items(int tiles, int nt_count) { return (ti
 
 // ------------------------------------------------------------- routed gate/up
 __global__ void __launch_bounds__(PF_NT, 2) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
-                                                      const int* __restrict__ tile_count, const int* __restrict__ perm,
+                                                      const int* __restrict__ tile_start, const int* __restrict__ perm,
                                                       LayerW L, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
   __shared__ __align__(16) uint4 a_lds[LDS_A1];
   __shared__ __align__(16) float rsum[PF_TM * (H / G)];
   __shared__ int rows[PF_TM];
   constexpr int NT = I / 128;
-  const int T = *tile_count;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
-    int ti, nt;
-    pf_item(q, NT, ti, nt);
-    if (ti >= T) continue;   // uniform over the workgroup
-    const int4 tl = tiles[ti];
+  // this XCD's tiles, the NT column slices of a tile on consecutive workgroups
+  const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * NT;
+  for (int q = blockIdx.x >> 3; q < items; q += gridDim.x >> 3) {
+    const int nt = q % NT;
+    const int4 tl = tiles[t0 + q / NT];
     const int e = tl.x, pos0 = tl.y, cnt = tl.z;
     wg_sync();   // the previous item is done with the LDS
     if (tid < PF_TM) rows[tid] = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
@@ -499,46 +537,157 @@ __global__ void __launch_bounds__(PF_NT, 2) k_pf_sh_gateup(const uint16_t* __res
 }
 
 // ------------------------------------------------------------- routed down
-// y[t * TOPK + slot][row] for every (token, slot) pair of each tile
-__global__ void __launch_bounds__(PF_NT) k_pf_down(const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo,
-                                                    const int4* __restrict__ tiles, const int* __restrict__ tile_count,
-                                                    const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A2];
-  __shared__ __align__(16) float rsum[PF_TM * (I / G)];
-  __shared__ int rows[PF_TM];
-  __shared__ int pairs[PF_TM];
-  constexpr int NT = H / 256;
-  const int T = *tile_count;
-  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
-    int ti, nt;
-    pf_item(q, NT, ti, nt);
-    if (ti >= T) continue;
-    const int4 tl = tiles[ti];
-    const int e = tl.x, pos0 = tl.y, cnt = tl.z;
-    wg_sync();
-    if (tid < PF_TM) {
-      rows[tid] = tid < cnt ? pos0 + tid : -1;
-      pairs[tid] = tid < cnt ? perm[pos0 + tid] : 0;
+// Work item: 32 rows of a tile (a half tile) x a quarter of the H output
+// columns.  The half tile's h rows (both bf16 parts, all of K = 512: 64 KB)
+// are staged into LDS once; each wave then streams the int4 rows of its 128
+// columns in blocks of 32, the codes of the next block in flight during the
+// MFMAs of the current one.  Output: y[pair][col] for each (token, slot) pair.
+constexpr int PD_TM = 32;              // rows of a half tile
+constexpr int PD_NQ = 4;               // column quarters of H per half tile
+constexpr int PD_NB = H / PD_NQ / 128; // 32-column blocks per wave (4 waves)
+constexpr int PD_KC = I / 8;           // 8-element chunks of a row (64)
+constexpr int PD_KG = I / G;           // K-groups (4)
+static_assert(PD_KC == 64 && PD_KG == 4 && PD_NB == 4, "routed down layout");
+
+// codes and scales of one lane's weight row: group g, bytes 32 hl + [0, 32)
+struct DownCodes {
+  uint4 c[PD_KG][2];
+  uint2 s;   // the row's 4 bf16 scales
+};
+
+__device__ __forceinline__ void down_load(const uint8_t* W, const uint16_t* S, int row, int hl, DownCodes& d) {
+  const uint4* p = reinterpret_cast<const uint4*>(W + (size_t)row * (I / 2)) + 2 * hl;
+#pragma unroll
+  for (int g = 0; g < PD_KG; ++g) {
+    d.c[g][0] = p[4 * g];
+    d.c[g][1] = p[4 * g + 1];
+  }
+  d.s = *reinterpret_cast<const uint2*>(S + (size_t)row * PD_KG);
+}
+
+// One 32 x 32 output block: rows of the half tile, columns of code block d.
+// a_lds[part][chunk][slot]: chunk c of tile row r at slot r ^ (c & 15).
+__device__ __forceinline__ pf_f32x16 down_block(const uint4 (*a_lds)[PD_KC][PD_TM], const DownCodes& d,
+                                                const uint4 (&rp)[3], int lrow, int hl) {
+  pf_f32x16 acc;
+#pragma unroll
+  for (int g = 0; g < PD_KG; ++g) {
+    pf_f32x16 temp;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 16 * g + 8 * hl + j;
+      const uint4 a0 = a_lds[0][c][lrow ^ (8 * hl + j)];
+      const uint4 a1 = a_lds[1][c][lrow ^ (8 * hl + j)];
+      const uint4 cw = d.c[g][j >> 2];
+      const uint32_t dw = (j & 3) == 0 ? cw.x : (j & 3) == 1 ? cw.y : (j & 3) == 2 ? cw.z : cw.w;
+      const uint4 bx = expand_codes(dw);
+      temp = mfma_bf16(a0, bx, j == 0 ? pf_f32x16{} : temp);
+      temp = mfma_bf16(a1, bx, temp);
+    }
+    const uint32_t sbits = (g & 1) ? ((g < 2 ? d.s.x : d.s.y) >> 16) : ((g < 2 ? d.s.x : d.s.y) & 0xFFFFu);
+    const float sc = bf16_bits_to_f32(sbits);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = g == 0 ? sc * temp[r] : fmaf(sc, temp[r], acc[r]);
+  }
+  // -136 sum_g s[n][g] R[m][g]: K = the 4 groups in lanes 0..31, zero-padded
+  const uint4 sb = hl == 0 ? make_uint4(d.s.x, d.s.y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+  pf_f32x16 corr = mfma_bf16(rp[0], sb, pf_f32x16{});
+  corr = mfma_bf16(rp[1], sb, corr);
+  corr = mfma_bf16(rp[2], sb, corr);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = fmaf(-136.f, corr[r], acc[r]);
+  return acc;
+}
+
+__global__ void __launch_bounds__(PF_NT, 2) k_pf_down(const uint16_t* __restrict__ h_hi,
+                                                       const uint16_t* __restrict__ h_lo,
+                                                       const int4* __restrict__ tiles, const int* __restrict__ tile_start,
+                                                       const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
+  __shared__ __align__(16) uint4 a_lds[2][PD_KC][PD_TM];
+  __shared__ float rsum[PD_TM][PD_KG];
+  __shared__ int pairs[PD_TM];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
+  // this XCD's half tiles, the column quarters of one on consecutive workgroups
+  const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * 2 * PD_NQ;
+  for (int q = blockIdx.x >> 3; q < items; q += gridDim.x >> 3) {
+    const int ht = q / PD_NQ, nq = q % PD_NQ;
+    const int4 tl = tiles[t0 + (ht >> 1)];
+    const int e = tl.x, pos = tl.y + PD_TM * (ht & 1), rows = min(tl.z - PD_TM * (ht & 1), PD_TM);
+    if (rows <= 0) continue;
+    const uint8_t* W = L.down + (size_t)e * H * (I / 2);
+    const uint16_t* S = L.down_s + (size_t)e * H * PD_KG;
+    const int n0 = nq * (H / PD_NQ) + wave * (PD_NB * 32);
+    wg_sync();   // the previous item is done with the LDS
+    // stage the half tile: thread = (chunk lane, rows wave + 4 i); padding rows
+    // read the first row
+    uint4 st[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave + 4 * i;
+      const size_t src = (size_t)(pos + (r < rows ? r : 0)) * I;
+      st[i][0] = reinterpret_cast<const uint4*>(h_hi + src)[lane];
+      st[i][1] = reinterpret_cast<const uint4*>(h_lo + src)[lane];
+    }
+    const int pr = tid < rows ? perm[pos + tid] : 0;
+    DownCodes c0, c1;
+    down_load(W, S, n0 + lrow, hl, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < PD_TM) pairs[tid] = pr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave + 4 * i;
+      a_lds[0][lane][r ^ (lane & 15)] = st[i][0];
+      a_lds[1][lane][r ^ (lane & 15)] = st[i][1];
+      float part = bf16x8_sum(st[i][0]) + bf16x8_sum(st[i][1]);
+      part += dpp_f32<DPP_XOR1>(part);   // the 16 chunks of one group
+      part += dpp_f32<DPP_XOR2>(part);
+      part += dpp_f32<DPP_HALF_MIRROR>(part);
+      part += dpp_f32<DPP_MIRROR>(part);
+      if ((lane & 15) == 0) rsum[r][lane >> 4] = part;
     }
     wg_sync();
-    const int wrow0 = nt * 256 + wave * 64;
-    const uint8_t* const W[1] = {L.down + (size_t)e * H * (I / 2)};
-    const uint16_t* const S[1] = {L.down_s + (size_t)e * H * (I / G)};
-    const uint16_t* const Ap[2] = {h_hi, h_lo};
-    pf_f32x16 acc[1][2][2] = {};
-    gemm_tile<2, 1, I / G, 2>(Ap, I, rows, W, S, wrow0, acc, a_lds, rsum);
+    // R of this lane's row split into three bf16 parts (exact products)
+    uint4 rp[3];
+    {
+      uint32_t w3[3][2] = {};
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int col = wrow0 + nb * 32 + lrow;
+      for (int g = 0; g < PD_KG; ++g) {
+        const float v = hl == 0 ? rsum[lrow][g] : 0.f;
+        const uint32_t b0 = f32_to_bf16_rne(v);
+        const float r1 = v - bf16_bits_to_f32(b0);
+        const uint32_t b1 = f32_to_bf16_rne(r1);
+        const uint32_t b2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1));
+        const int sh = 16 * (g & 1);
+        w3[0][g >> 1] |= b0 << sh;
+        w3[1][g >> 1] |= b1 << sh;
+        w3[2][g >> 1] |= b2 << sh;
+      }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = tile_row(mb, r);
-          if (m < cnt) y[(size_t)pairs[m] * H + col] = acc[0][nb][mb][r];
-        }
+      for (int k = 0; k < 3; ++k) rp[k] = make_uint4(w3[k][0], w3[k][1], 0u, 0u);
     }
+    auto store = [&](int nb, const pf_f32x16& acc) {
+      const int col = n0 + nb * 32 + lrow;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = tile_row(0, r);
+        if (m < rows) y[(size_t)pairs[m] * H + col] = acc[r];
+      }
+    };
+    // four column blocks, two code sets in turn (no register copies while a
+    // load is in flight)
+    down_load(W, S, n0 + 32 + lrow, hl, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(0, down_block(a_lds, c0, rp, lrow, hl));
+    __builtin_amdgcn_sched_barrier(0);
+    down_load(W, S, n0 + 64 + lrow, hl, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    store(1, down_block(a_lds, c1, rp, lrow, hl));
+    __builtin_amdgcn_sched_barrier(0);
+    down_load(W, S, n0 + 96 + lrow, hl, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(2, down_block(a_lds, c0, rp, lrow, hl));
+    __builtin_amdgcn_sched_barrier(0);
+    store(3, down_block(a_lds, c1, rp, lrow, hl));
   }
 }
 
@@ -593,7 +742,7 @@ __global__ void __launch_bounds__(PF_NT) k_pf_sh_down(const float* xin, float* o
 int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc) {
   const size_t T = FLINT_MAX_TOKENS, P = T * TOPK;
   const size_t sizes[14] = {T * H * 2,      T * E * 4,  T * TOPK * 4, T * TOPK * 4, (size_t)E * PF_BW * 4,
-                            (size_t)(E + 1) * 4, (size_t)PF_MAX_TILES * 16, 4, P * 4, P * I * 2,
+                            (size_t)(E + 1) * 4, (size_t)PF_MAX_TILES * 16, 9 * 4, P * 4, P * I * 2,
                             P * I * 2,      P * H * 4,  T * IS * 2,   T * IS * 2};
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t tot = 0;
@@ -603,7 +752,7 @@ int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc) {
   if (rc) return rc;
   *mem = p;
   void** dst[14] = {(void**)&ws->a,     (void**)&ws->z,       (void**)&ws->ids,   (void**)&ws->w,
-                    (void**)&ws->bitmap, (void**)&ws->offsets, (void**)&ws->tiles, (void**)&ws->tile_count,
+                    (void**)&ws->bitmap, (void**)&ws->offsets, (void**)&ws->tiles, (void**)&ws->tile_start,
                     (void**)&ws->perm,  (void**)&ws->h_hi,    (void**)&ws->h_lo,  (void**)&ws->y,
                     (void**)&ws->hs_hi, (void**)&ws->hs_lo};
   for (int i = 0; i < 14; ++i) {
@@ -616,23 +765,23 @@ int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc) {
 hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const PrefillWS& ws,
                                 int* trace_ids, float* trace_w, hipStream_t s) {
   if (n <= DECODE_MAX_TOKENS || n > FLINT_MAX_TOKENS) return hipErrorInvalidValue;
-  const int tiles_max = (n * TOPK + PF_TM - 1) / PF_TM + E;   // <= PF_MAX_TILES
   const int mt = (n + PF_TM - 1) / PF_TM;
   hipLaunchKernelGGL(k_pf_input, dim3(n), dim3(PF_NT), 0, s, xin, n, ws.a, ws.bitmap);
   hipLaunchKernelGGL(k_pf_router, dim3((n + 31) / 32, E / 128), dim3(PF_NT), 0, s, ws.a, n, L.router, ws.z);
   hipLaunchKernelGGL(k_pf_route, dim3((n + 3) / 4), dim3(PF_NT), 0, s, ws.z, n, L.bias, ws.ids, ws.w, ws.bitmap,
                      trace_ids, trace_w);
-  hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_count);
+  hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_start);
   hipLaunchKernelGGL(k_pf_scatter, dim3((n * TOPK + PF_NT - 1) / PF_NT), dim3(PF_NT), 0, s, ws.ids, n, ws.bitmap,
                      ws.offsets, ws.perm);
   // persistent grids: about one round of resident workgroups, at most one per item
   auto grid = [](int items, int resident) { return dim3(std::max(1, std::min(items, resident))); };
-  hipLaunchKernelGGL(k_pf_gateup, grid(pf_items(tiles_max, I / 128), 2 * 256), dim3(PF_NT), 0, s, ws.a, ws.tiles,
-                     ws.tile_count, ws.perm, L, ws.h_hi, ws.h_lo);
+  // routed GEMMs: two resident workgroups per CU, 64 per XCD (a multiple of 8)
+  hipLaunchKernelGGL(k_pf_gateup, dim3(2 * 256), dim3(PF_NT), 0, s, ws.a, ws.tiles, ws.tile_start, ws.perm, L,
+                     ws.h_hi, ws.h_lo);
   hipLaunchKernelGGL(k_pf_sh_gateup, grid(pf_items(mt, IS / 128), 2 * 256), dim3(PF_NT), 0, s, ws.a, n, L, ws.hs_hi,
                      ws.hs_lo);
-  hipLaunchKernelGGL(k_pf_down, grid(pf_items(tiles_max, H / 256), 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo,
-                     ws.tiles, ws.tile_count, ws.perm, L, ws.y);
+  hipLaunchKernelGGL(k_pf_down, dim3(2 * 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles, ws.tile_start, ws.perm,
+                     L, ws.y);
   hipLaunchKernelGGL(k_pf_sh_down, grid(pf_items(mt, H / 256), 256), dim3(PF_NT), 0, s, xin, out, n, ws.hs_hi,
                      ws.hs_lo, L, ws.w, ws.y);
   return hipGetLastError();
