@@ -114,24 +114,35 @@ __global__ void __launch_bounds__(PF_NT) k_pf_input(const float* __restrict__ x,
 }
 
 // ------------------------------------------------------------- router GEMM
-// 32 tokens x 128 experts per workgroup, 32 experts per wave, K = 2048.
+// 32 tokens x 32 experts per workgroup.  Wave w sums K in [512 w, 512 w + 512)
+// with two interleaved accumulators (short dependency chains), and the four
+// partial sums are added in wave order.
 __global__ void __launch_bounds__(PF_NT) k_pf_router(const uint16_t* __restrict__ a, int n,
                                                       const uint16_t* __restrict__ router, float* __restrict__ z) {
+  __shared__ float part[3][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lrow = lane & 31, hl = lane >> 5;
-  const int m0 = blockIdx.x * 32, e = blockIdx.y * 128 + wave * 32 + lrow;
+  const int m0 = blockIdx.x * 32, e = blockIdx.y * 32 + lrow;
   const int m = min(m0 + lrow, n - 1);   // rows past n repeat the last token and are not stored
-  const uint4* ar = reinterpret_cast<const uint4*>(a + (size_t)m * H);
-  const uint4* wr = reinterpret_cast<const uint4*>(router + (size_t)e * H);
-  pf_f32x16 acc = {};
-#pragma unroll 8
-  for (int j = 0; j < H / 16; ++j) {
-    const int c = 2 * j + hl;   // 8-element chunk of this lane in MFMA step j
-    acc = mfma_bf16(ar[c], to_pair_order(wr[c]), acc);
+  const uint4* ar = reinterpret_cast<const uint4*>(a + (size_t)m * H) + wave * 64 + hl;
+  const uint4* wr = reinterpret_cast<const uint4*>(router + (size_t)e * H) + wave * 64 + hl;
+  pf_f32x16 acc0 = {}, acc1 = {};
+#pragma unroll 4
+  for (int j = 0; j < 32; j += 2) {   // MFMA step j: chunks 2 j (lanes 0..31) and 2 j + 1 (lanes 32..63)
+    acc0 = mfma_bf16(ar[2 * j], to_pair_order(wr[2 * j]), acc0);
+    acc1 = mfma_bf16(ar[2 * j + 2], to_pair_order(wr[2 * j + 2]), acc1);
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int mm = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-    if (mm < n) z[(size_t)mm * E + e] = acc[r];
+    for (int r = 0; r < 16; ++r) part[wave - 1][r][lane] = acc0[r] + acc1[r];
+  }
+  wg_sync();
+  if (wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (((acc0[r] + acc1[r]) + part[0][r][lane]) + part[1][r][lane]) + part[2][r][lane];
+      const int mm = m0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (mm < n) z[(size_t)mm * E + e] = v;
+    }
   }
 }
 
@@ -767,7 +778,7 @@ hipError_t launch_prefill_layer(const float* xin, float* out, int n, const Layer
   if (n <= DECODE_MAX_TOKENS || n > FLINT_MAX_TOKENS) return hipErrorInvalidValue;
   const int mt = (n + PF_TM - 1) / PF_TM;
   hipLaunchKernelGGL(k_pf_input, dim3(n), dim3(PF_NT), 0, s, xin, n, ws.a, ws.bitmap);
-  hipLaunchKernelGGL(k_pf_router, dim3((n + 31) / 32, E / 128), dim3(PF_NT), 0, s, ws.a, n, L.router, ws.z);
+  hipLaunchKernelGGL(k_pf_router, dim3((n + 31) / 32, E / 32), dim3(PF_NT), 0, s, ws.a, n, L.router, ws.z);
   hipLaunchKernelGGL(k_pf_route, dim3((n + 3) / 4), dim3(PF_NT), 0, s, ws.z, n, L.bias, ws.ids, ws.w, ws.bitmap,
                      trace_ids, trace_w);
   hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_start);
