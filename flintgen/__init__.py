@@ -42,7 +42,13 @@ T_GATE_S, T_UP_S, T_DOWN_S = 3, 4, 5
 T_SH_GATE, T_SH_UP, T_SH_DOWN = 6, 7, 8
 T_SH_GATE_S, T_SH_UP_S, T_SH_DOWN_S = 9, 10, 11
 T_ROUTER, T_BIAS = 12, 13
+# the model's other int4 matrices: the dense MLP of layers 0 and 1, the head
+T_DENSE_GATE, T_DENSE_UP, T_DENSE_DOWN = 14, 15, 16
+T_DENSE_GATE_S, T_DENSE_UP_S, T_DENSE_DOWN_S = 17, 18, 19
+T_HEAD, T_HEAD_S = 20, 21
 TOKEN_BASE = 1_000_000
+DENSE_MLP_SIZE = 6144   # config table row "Dense MLP size" (layers 0 and 1)
+VOCAB = 150144          # config table row "Vocabulary": rows of the output head
 
 
 @dataclasses.dataclass(frozen=True)
@@ -112,6 +118,12 @@ def _words(keys, n: int, device) -> torch.Tensor:
     k2 = torch.tensor([k[1] for k in keys], dtype=torch.int64, device=device)[:, None]
     i = torch.arange(n, dtype=torch.int64, device=device)[None, :]
     return lowbias32(lowbias32((i + k1) & MASK32) ^ k2)
+
+
+def _words_at(key, idx: torch.Tensor) -> torch.Tensor:
+    """Words at the given indices (int64 tensor) of one block."""
+    k1, k2 = key
+    return lowbias32(lowbias32((idx + k1) & MASK32) ^ k2)
 
 
 def _words_to_bytes(w: torch.Tensor) -> torch.Tensor:
@@ -282,6 +294,42 @@ class Synth:
         out["router"] = self.router(layer).to(device)
         out["bias"] = self.bias(layer).to(device)
         return out
+
+
+def q4_matrix(seed: int, layer: int, tensor: int, scale_tensor: int, rows: int, k: int, group: int = 128,
+              device="cpu", row_ids=None):
+    """One int4 matrix [rows][k] of the same distributions as the experts:
+    codes uint8 [r][k/2] and bf16 scale bits int16 [r][k/group].  ``row_ids``
+    (a sequence of row indices) generates only those rows; each row's bytes
+    do not depend on which other rows are generated."""
+    wc, ws = k // 8, k // group
+    kc = block_key(seed, layer, tensor, 0)
+    ks = block_key(seed, layer, scale_tensor, 0)
+    if row_ids is None:
+        codes = _words_to_bytes(_words([kc], rows * wc, device)).reshape(rows, k // 2)
+        scales = _scales_from_words(_words([ks], rows * ws, device)).reshape(rows, ws)
+        return codes, scales
+    r = torch.as_tensor(list(row_ids), dtype=torch.int64, device=device)[:, None]
+    if bool(((r < 0) | (r >= rows)).any()):
+        raise ValueError("row index out of range")
+    codes = _words_to_bytes(_words_at(kc, r * wc + torch.arange(wc, device=device)[None, :]))
+    scales = _scales_from_words(_words_at(ks, r * ws + torch.arange(ws, device=device)[None, :]))
+    return codes.reshape(len(r), k // 2), scales.reshape(len(r), ws)
+
+
+def dense_layer(seed: int, layer: int, device="cpu", hidden: int = FLINT.hidden, inter: int = DENSE_MLP_SIZE,
+                group: int = 128):
+    """Dense SwiGLU MLP of model layer 0 or 1: gate/up codes [inter][hidden/2],
+    scales [inter][hidden/G]; down codes [hidden][inter/2], scales [hidden][inter/G]."""
+    g = q4_matrix(seed, layer, T_DENSE_GATE, T_DENSE_GATE_S, inter, hidden, group, device)
+    u = q4_matrix(seed, layer, T_DENSE_UP, T_DENSE_UP_S, inter, hidden, group, device)
+    d = q4_matrix(seed, layer, T_DENSE_DOWN, T_DENSE_DOWN_S, hidden, inter, group, device)
+    return {"gate": g[0], "gate_s": g[1], "up": u[0], "up_s": u[1], "down": d[0], "down_s": d[1]}
+
+
+def head(seed: int, device="cpu", rows: int = VOCAB, hidden: int = FLINT.hidden, group: int = 128, row_ids=None):
+    """Output head [rows][hidden] int4: (codes, scale bits); ``row_ids`` as in q4_matrix."""
+    return q4_matrix(seed, 0, T_HEAD, T_HEAD_S, rows, hidden, group, device, row_ids)
 
 
 def token(seed: int, t: int, hidden: int = FLINT.hidden) -> np.ndarray:

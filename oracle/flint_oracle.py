@@ -241,6 +241,42 @@ def moe_stack(x0, src, shape, layer_begin: int, layer_end: int,
     return recs
 
 
+# ------------------------------------------------------------------ dense layers and head
+# The model's other int4 matrix-vector products read per decode token (How to
+# Run Flint Locally, "The architecture, from config.json": layers 0 and 1 have
+# a dense MLP of size 6,144; "One decode step in bytes": every token reads the
+# whole 150,144 x 2,048 output head, which the announcement quoted there keeps
+# at 4 bits).  Readings: the dense MLP is the same SwiGLU as an expert, fed by
+# the same block input (bf16 of the RMS-normalised residual) and added to the
+# residual; the head is fed by the same normalisation and rounding of the final
+# residual (epsilon 1e-6, gain 1), and its logits are fp64 here.
+
+@dataclasses.dataclass
+class DenseResult:
+    delta: np.ndarray      # Wd h (fp64)
+    h: np.ndarray          # silu(Wg a) * (Wu a) (fp64)
+    x_out: np.ndarray      # fp32(x + delta)
+
+
+def dense_mlp(x, w, shape) -> DenseResult:
+    """x + Wd (silu(Wg a) * (Wu a)) with a = bf16(rmsnorm(x)); ``w`` holds
+    gate/up codes [inter][H/2] and down codes [H][inter/2] with their scales."""
+    a = block_input(x, shape)
+    w = {k: np.asarray(v) for k, v in w.items()}
+    y, h = swiglu_expert(dequant(w["gate"], w["gate_s"], shape.group),
+                         dequant(w["up"], w["up_s"], shape.group),
+                         dequant(w["down"], w["down_s"], shape.group), a)
+    x_out = (np.asarray(x, dtype=np.float32).astype(np.float64) + y).astype(np.float32)
+    return DenseResult(delta=y, h=h, x_out=x_out)
+
+
+def head_logits(x, codes, scales, shape) -> np.ndarray:
+    """logits[r] = sum_k W[r, k] a[k] in fp64 with a = bf16(rmsnorm(x)), for
+    the rows given (codes [rows][H/2], scale bits [rows][H/G])."""
+    a = block_input(x, shape)
+    return dequant(np.asarray(codes), np.asarray(scales), shape.group) @ a
+
+
 # ------------------------------------------------------------------ counts
 def parameter_counts(shape, n_layers: int):
     """Per-token parameter counts read by one decode step of the MoE layers:

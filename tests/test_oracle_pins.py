@@ -377,13 +377,13 @@ def test_parameter_counts_match_the_pages():
         check(name, c[name])
     H = FLINT.hidden
     attention = 49 * (H * 4096 + 2 * H * 512 + 4096 * H)
-    dense = 2 * 3 * H * 6144
+    dense = 2 * 3 * H * fg.DENSE_MLP_SIZE
     check("attention_total", attention)
     check("dense_mlp_total", dense)
     moe = c["routed_per_token"] + c["shared_per_token"] + c["router_per_token"]
     rest = gold["body_total"]["printed"] - attention - dense - moe
     check("norms_and_sinks", rest)
-    assert 150144 * H == gold["lm_head"]["printed"]
+    assert fg.VOCAB * H == gold["lm_head"]["printed"]
     assert gold["body_total"]["printed"] + gold["lm_head"]["printed"] == gold["active_total"]["printed"]
     # bytes one token reads per layer in this build's int4 format
     assert O.bytes_per_token_layer(FLINT) == 14_025_728
