@@ -29,8 +29,12 @@ FLINT_ERR_HIP = -3
 FLINT_ERR_UNSUPPORTED = -4
 FLINT_ERR_DEVICE = -5
 
+FLINT_DENSE_MLP_SIZE = 6144
+FLINT_VOCAB = 150144
+FLINT_DENSE_MAX_TOKENS = 16
+
 EXPORTED = ("flint_moe_create", "flint_moe_forward", "flint_moe_set_trace", "flint_moe_status",
-            "flint_moe_destroy", "flint_moe_last_error")
+            "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward", "flint_head_forward")
 
 
 class flint_q4(ctypes.Structure):
@@ -72,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_destroy.restype = None
         L.flint_moe_last_error.argtypes = []
         L.flint_moe_last_error.restype = ctypes.c_char_p
+        L.flint_dense_mlp_forward.argtypes = [flint_q4, flint_q4, flint_q4, ci, vp, ci, vp, vp, vp]
+        L.flint_dense_mlp_forward.restype = ci
+        L.flint_head_forward.argtypes = [flint_q4, ci, vp, ci, vp, vp]
+        L.flint_head_forward.restype = ci
         _lib = L
     return _lib
 
@@ -127,6 +135,21 @@ def flint_moe_destroy(h) -> None:
 
 def flint_moe_last_error() -> str:
     return lib().flint_moe_last_error().decode()
+
+
+def q4(codes, scales) -> flint_q4:
+    """Descriptor of one int4 matrix (device tensors or addresses)."""
+    return flint_q4(_ptr(codes), _ptr(scales))
+
+
+def flint_dense_mlp_forward(gate, up, down, inter, x, n_tokens, h, out, stream=None) -> None:
+    """gate, up, down: flint_q4 descriptors (see q4)."""
+    _check(lib().flint_dense_mlp_forward(gate, up, down, inter, _ptr(x), n_tokens, _ptr(h), _ptr(out),
+                                         _stream(stream)))
+
+
+def flint_head_forward(head, rows, x, n_tokens, logits, stream=None) -> None:
+    _check(lib().flint_head_forward(head, rows, _ptr(x), n_tokens, _ptr(logits), _stream(stream)))
 
 
 def _stream(stream):

@@ -9,6 +9,7 @@
 
 #include "decode.h"
 #include "decode_persistent.h"
+#include "dense.h"
 #include "prefill.h"
 
 using namespace flint;
@@ -298,5 +299,57 @@ int flint_moe_status(flint_moe_t h, void* stream) {
 }
 
 void flint_moe_destroy(flint_moe_t h) { release(h); }
+
+// ------------------------------------------------------------- dense MLP and head
+static bool misaligned16(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char *pa = (const char*)a, *pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+static int check_q4(flint_q4 m, const char* name) {
+  if (!m.codes || !m.scales) return fail(FLINT_ERR_INVALID_ARG, "%s: codes or scales is NULL", name);
+  if (misaligned16(m.codes)) return fail(FLINT_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned", name);
+  if ((uintptr_t)m.scales & 1) return fail(FLINT_ERR_INVALID_ARG, "%s: scales must be 2-byte aligned", name);
+  return FLINT_OK;
+}
+
+int flint_dense_mlp_forward(flint_q4 gate, flint_q4 up, flint_q4 down, int inter, const float* x, int n_tokens,
+                            float* h, float* out, void* stream) {
+  int rc;
+  if ((rc = check_q4(gate, "gate")) || (rc = check_q4(up, "up")) || (rc = check_q4(down, "down"))) return rc;
+  if (!x || !h || !out) return fail(FLINT_ERR_INVALID_ARG, "x, h or out is NULL");
+  if (misaligned16(x) || misaligned16(h) || misaligned16(out))
+    return fail(FLINT_ERR_INVALID_ARG, "x, h and out must be 16-byte aligned");
+  if (n_tokens < 1 || n_tokens > FLINT_DENSE_MAX_TOKENS)
+    return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_DENSE_MAX_TOKENS);
+  if (inter < 2048 || inter > FLINT_DENSE_MLP_SIZE || inter % 2048)
+    return fail(FLINT_ERR_INVALID_ARG, "inter = %d: a multiple of 2048 up to %d is required", inter,
+                FLINT_DENSE_MLP_SIZE);
+  const size_t xb = (size_t)n_tokens * H * sizeof(float), hb = (size_t)n_tokens * inter * sizeof(float);
+  if ((const void*)x != (const void*)out && overlap(x, xb, out, xb))
+    return fail(FLINT_ERR_INVALID_ARG, "x and out overlap partially");
+  if (overlap(h, hb, x, xb) || overlap(h, hb, out, xb)) return fail(FLINT_ERR_INVALID_ARG, "h overlaps x or out");
+  const hipError_t e = launch_dense_mlp(gate.codes, gate.scales, up.codes, up.scales, down.codes, down.scales, inter,
+                                        x, n_tokens, h, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "dense MLP launch");
+  return FLINT_OK;
+}
+
+int flint_head_forward(flint_q4 head, int rows, const float* x, int n_tokens, float* logits, void* stream) {
+  int rc;
+  if ((rc = check_q4(head, "head"))) return rc;
+  if (!x || !logits) return fail(FLINT_ERR_INVALID_ARG, "x or logits is NULL");
+  if (misaligned16(x) || misaligned16(logits)) return fail(FLINT_ERR_INVALID_ARG, "x and logits must be 16-byte aligned");
+  if (n_tokens < 1 || n_tokens > FLINT_DENSE_MAX_TOKENS)
+    return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_DENSE_MAX_TOKENS);
+  if (rows < 1) return fail(FLINT_ERR_INVALID_ARG, "rows = %d must be positive", rows);
+  if (overlap(x, (size_t)n_tokens * H * sizeof(float), logits, (size_t)n_tokens * rows * sizeof(float)))
+    return fail(FLINT_ERR_INVALID_ARG, "logits overlaps x");
+  const hipError_t e = launch_head(head.codes, head.scales, rows, x, n_tokens, logits, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "head launch");
+  return FLINT_OK;
+}
 
 }  // extern "C"

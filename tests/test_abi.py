@@ -1,5 +1,5 @@
-"""The C-ABI library: it loads, exports every function include/flint_moe.h
-declares, and rejects invalid arguments before touching the GPU."""
+"""The C-ABI library: it loads, exports every function include/*.h declares,
+and rejects invalid arguments before touching the GPU."""
 import ctypes
 import os
 import re
@@ -8,13 +8,17 @@ import pytest
 
 import int4_expert_ffn_amd as F
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "flint_moe.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "flint_moe.h")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(flint_moe_\w+)\s*\(", text)))
+    names = set()
+    for hdr in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+        names |= set(re.findall(r"\b(flint_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_names():
@@ -32,6 +36,10 @@ def test_constants_match_header():
     for name in ("FLINT_HIDDEN", "FLINT_EXPERTS", "FLINT_EXPERT_SIZE", "FLINT_SHARED_SIZE", "FLINT_TOP_K",
                  "FLINT_GROUP", "FLINT_MAX_LAYERS", "FLINT_MAX_TOKENS", "FLINT_OK", "FLINT_ERR_INVALID_ARG",
                  "FLINT_ERR_OUT_OF_MEMORY", "FLINT_ERR_HIP", "FLINT_ERR_UNSUPPORTED", "FLINT_ERR_DEVICE"):
+        m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(F, name), name
+    text = open(os.path.join(INCLUDE, "flint_dense.h")).read()
+    for name in ("FLINT_DENSE_MLP_SIZE", "FLINT_VOCAB", "FLINT_DENSE_MAX_TOKENS"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(F, name), name
 
@@ -57,3 +65,36 @@ def test_null_handle_calls():
     lib.flint_moe_destroy(None)          # NULL-safe
     with pytest.raises(F.FlintMoEError):
         F.flint_moe_forward(None, 16, 1, 0, 1, 16)
+
+
+def test_dense_and_head_reject_bad_arguments_before_any_hip_call():
+    """Fake but aligned addresses: every call fails validation, so nothing is
+    enqueued and no GPU is needed."""
+    lib = F.lib()
+    A = 1 << 20
+    good = F.q4(A, A)
+    inval = F.FLINT_ERR_INVALID_ARG
+    H, W = F.FLINT_HIDDEN, F.FLINT_DENSE_MLP_SIZE
+    x, h, out = 16 * A, 32 * A, 48 * A
+    # dense MLP
+    assert lib.flint_dense_mlp_forward(F.q4(None, A), good, good, W, x, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(F.q4(A + 8, A), good, good, W, x, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(F.q4(A, A + 1), good, good, W, x, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(good, good, good, W, None, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(good, good, good, W, x + 4, 1, h, out, None) == inval
+    for n in (0, F.FLINT_DENSE_MAX_TOKENS + 1):
+        assert lib.flint_dense_mlp_forward(good, good, good, W, x, n, h, out, None) == inval
+    for inter in (0, 1024, 3000, W + 2048):
+        assert lib.flint_dense_mlp_forward(good, good, good, inter, x, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(good, good, good, W, x, 2, h, x + 16 * 4, None) == inval   # partial overlap
+    assert lib.flint_dense_mlp_forward(good, good, good, W, x, 1, x + 4 * H - 16, x, None) == inval   # h overlaps
+    assert "overlap" in F.flint_moe_last_error()
+    # head
+    assert lib.flint_head_forward(F.q4(A, None), 10, x, 1, out, None) == inval
+    assert lib.flint_head_forward(good, 0, x, 1, out, None) == inval
+    assert lib.flint_head_forward(good, 10, x, 0, out, None) == inval
+    assert lib.flint_head_forward(good, 10, x, 17, out, None) == inval
+    assert lib.flint_head_forward(good, 10, x + 8, 1, out, None) == inval
+    assert lib.flint_head_forward(good, 10, x, 1, x + 64, None) == inval
+    with pytest.raises(F.FlintMoEError):
+        F.flint_head_forward(good, 0, x, 1, out)

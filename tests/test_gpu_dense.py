@@ -1,0 +1,149 @@
+"""GPU parity of the output head and of the dense SwiGLU MLP of layers 0 and 1
+(int4 matrix-vector products, up to 16 tokens) against the CPU oracle.
+
+Error bounds come from the arithmetic: each code x activation product is exact
+in fp32, and a logit (or a gate/up/down row) is an fp32 sum of 2,048 (6,144)
+such terms of the form (code + 136) s a, computed as 64 lane sums of 32 terms
+then a 6-level tree.  The rounding error is below 3e-6 of the sum of the
+terms' magnitudes; the tests allow 1e-5 of it per value, and 1e-5 rel-L2 per
+token on the dense MLP's residual update (the decode bound).
+"""
+import numpy as np
+import pytest
+import torch
+
+import flintgen as fg
+import int4_expert_ffn_amd as F
+from oracle import flint_oracle as O
+
+pytestmark = pytest.mark.gpu
+FL = fg.FLINT
+H = FL.hidden
+REL_L2 = 1e-5
+
+
+def magnitude_bound(codes, scales, a):
+    """sum_k |(code + 136) s a_k| per row: the scale of the fp32 rounding error."""
+    v = O.unpack_int4(codes).astype(np.float64) + 136.0
+    s = np.repeat(O.bf16_bits_to_f64(scales), FL.group, axis=-1)
+    return np.abs(v * s) @ np.abs(a)
+
+
+# ------------------------------------------------------------------ head
+@pytest.fixture(scope="module")
+def head():
+    c, s = fg.head(0, device="cuda")
+    torch.cuda.synchronize()
+    return c, s
+
+
+def run_head(c, s, rows, x_np):
+    x = torch.from_numpy(np.ascontiguousarray(x_np, np.float32)).cuda()
+    out = torch.full((x.shape[0], rows), float("nan"), dtype=torch.float32, device="cuda")
+    F.flint_head_forward(F.q4(c, s), rows, x, x.shape[0], out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_head_rows(x_np, logits, rows_idx, codes, scales):
+    for t in range(x_np.shape[0]):
+        ref = O.head_logits(x_np[t], codes, scales, FL)
+        bound = 1e-5 * magnitude_bound(codes, scales, O.block_input(x_np[t], FL))
+        err = np.abs(logits[t, rows_idx].astype(np.float64) - ref)
+        assert np.all(err <= bound), (t, float(np.max(err / bound)))
+
+
+def test_head_full_vocabulary_sampled_rows(head):
+    c, s = head
+    rng = np.random.default_rng(0)
+    idx = np.unique(np.concatenate([np.arange(8), fg.VOCAB - 8 + np.arange(8), rng.choice(fg.VOCAB, 48, replace=False)]))
+    cc, ss = fg.head(0, row_ids=idx.tolist())
+    x = fg.tokens(0, range(40, 44))
+    out = run_head(c, s, fg.VOCAB, x)
+    assert np.all(np.isfinite(out))
+    check_head_rows(x, out, idx, cc.numpy(), ss.numpy())
+
+
+@pytest.mark.parametrize("rows", [1, 3, 1000, 4097])
+def test_head_ragged_row_counts_every_row(head, rows):
+    c, s = head
+    cc, ss = fg.head(0, rows=rows)
+    x = fg.tokens(1, range(3))
+    out = run_head(c, s, rows, x)
+    check_head_rows(x, out, np.arange(rows), cc.numpy(), ss.numpy())
+
+
+def test_head_batch_invariance_and_zero_input(head):
+    c, s = head
+    x = fg.tokens(2, range(16))
+    singles = np.stack([run_head(c, s, fg.VOCAB, x[t:t + 1])[0] for t in (0, 5, 15)])
+    full = run_head(c, s, fg.VOCAB, x)
+    assert np.array_equal(full[[0, 5, 15]], singles)
+    assert np.array_equal(run_head(c, s, fg.VOCAB, x[:4])[[0]], singles[[0]])
+    z = run_head(c, s, 4097, np.zeros((2, H), np.float32))
+    assert np.all(z == 0)
+
+
+# ------------------------------------------------------------------ dense MLP
+@pytest.fixture(scope="module", params=[fg.DENSE_MLP_SIZE, 2048])
+def dense(request):
+    inter = request.param
+    w = fg.dense_layer(0, 1, device="cuda", inter=inter)
+    torch.cuda.synchronize()
+    wc = {k: v.cpu().numpy() for k, v in w.items()}
+    return inter, w, wc
+
+
+def run_dense(inter, w, x_np, out_is_x=False):
+    x = torch.from_numpy(np.ascontiguousarray(x_np, np.float32)).cuda()
+    n = x.shape[0]
+    h = torch.full((n, inter), float("nan"), dtype=torch.float32, device="cuda")
+    out = x if out_is_x else torch.full_like(x, float("nan"))
+    F.flint_dense_mlp_forward(F.q4(w["gate"], w["gate_s"]), F.q4(w["up"], w["up_s"]), F.q4(w["down"], w["down_s"]),
+                              inter, x, n, h, out)
+    torch.cuda.synchronize()
+    return h.cpu().numpy(), out.cpu().numpy()
+
+
+def test_dense_mlp_parity(dense):
+    inter, w, wc = dense
+    x = fg.tokens(3, range(5))
+    h, out = run_dense(inter, w, x)
+    for t in range(len(x)):
+        res = O.dense_mlp(x[t], wc, FL)
+        a = O.block_input(x[t], FL)
+        # h: silu(g) u from two rows with the bound above (silu is 1-Lipschitz-ish: |silu'| <= 1.1)
+        bg = magnitude_bound(wc["gate"], wc["gate_s"], a)
+        bu = magnitude_bound(wc["up"], wc["up_s"], a)
+        g = O.dequant(wc["gate"], wc["gate_s"], FL.group) @ a
+        u = O.dequant(wc["up"], wc["up_s"], FL.group) @ a
+        hb = 1e-5 * (1.1 * bg * np.abs(u) + np.abs(O.silu(g)) * bu) + 1e-6 * np.abs(res.h)
+        assert np.all(np.abs(h[t] - res.h) <= hb), (t, float(np.max(np.abs(h[t] - res.h) / hb)))
+        d_gpu = out[t].astype(np.float64) - x[t]
+        d_ref = res.x_out.astype(np.float64) - x[t]
+        err = np.linalg.norm(d_gpu - d_ref) / np.linalg.norm(d_ref)
+        assert err <= REL_L2, (t, err)
+    print(f"inter={inter}: max |h| {np.abs(h).max():.3g}")
+
+
+def test_dense_mlp_batch_invariance_in_place_and_zero(dense):
+    inter, w, wc = dense
+    x = fg.tokens(4, range(16))
+    h1, o1 = run_dense(inter, w, x[:1])
+    h7, o7 = run_dense(inter, w, x[:7])
+    h16, o16 = run_dense(inter, w, x)
+    assert np.array_equal(h16[:1], h1) and np.array_equal(o16[:1], o1)
+    assert np.array_equal(h16[:7], h7) and np.array_equal(o16[:7], o7)
+    hi, oi = run_dense(inter, w, x, out_is_x=True)
+    assert np.array_equal(hi, h16) and np.array_equal(oi, o16)
+    hz, oz = run_dense(inter, w, np.zeros((3, H), np.float32))
+    assert np.all(hz == 0) and np.all(oz == 0)
+
+
+def test_dense_mlp_power_of_two_up_scale_is_exact(dense):
+    inter, w, wc = dense
+    x = fg.tokens(5, range(2))
+    h, _ = run_dense(inter, w, x)
+    w2 = dict(w, up_s=(w["up_s"].to(torch.int32) + (3 << 7)).to(torch.int16))
+    h2, _ = run_dense(inter, w2, x)
+    assert np.array_equal(h2, h * 8.0)
