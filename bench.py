@@ -282,6 +282,76 @@ def bench_cost_table(args):
                       "table": rows}), flush=True)
 
 
+def q4_matrix_bytes(rows, k):
+    return rows * (k // 2) + rows * (k // G) * 2
+
+
+def bench_head_dense(args):
+    """The model's other int4 GEMVs at batch 1: the output head (150,144 x 2,048)
+    and the dense SwiGLU MLP of layers 0 and 1 (width 6,144).  Timed launches
+    rotate through enough copies of the weights that the 256 MB last-level
+    cache cannot hold them, so every launch streams its weights from HBM."""
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    dev = torch.device("cuda:0")
+    rows, inter = fg.VOCAB, fg.DENSE_MLP_SIZE
+    heads = [fg.head(0, device=dev) for _ in range(3)]                     # 3 x 158.5 MB
+    denses = [fg.dense_layer(0, i % 2, device=dev) for i in range(16)]     # 16 x 19.5 MB
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
+    logits = torch.empty((16, rows), dtype=torch.float32, device=dev)
+    hbuf = torch.empty((16, inter), dtype=torch.float32, device=dev)
+    xo = torch.empty((16, H), dtype=torch.float32, device=dev)
+
+    def head_call(i, n):
+        c, sc = heads[i % len(heads)]
+        F.flint_head_forward(F.q4(c, sc), rows, pool[i % 48:i % 48 + n], n, logits, stream)
+
+    def dense_call(i, n):
+        w = denses[i % len(denses)]
+        F.flint_dense_mlp_forward(F.q4(w["gate"], w["gate_s"]), F.q4(w["up"], w["up_s"]), F.q4(w["down"], w["down_s"]),
+                                  inter, pool[i % 48:i % 48 + n], n, hbuf, xo, stream)
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i, n)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn(i, n)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        return float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+    head_bytes = q4_matrix_bytes(rows, H)
+    dense_bytes = 2 * q4_matrix_bytes(inter, H) + q4_matrix_bytes(H, inter)
+    res_head = {n: timed(head_call, n) for n in (1, 4, 16)}
+    res_dense = {n: timed(dense_call, n) for n in (1, 4, 16)}
+    med = res_head[1][0]
+    achieved = (head_bytes + rows * 4 + H * 4) / med / 1e9
+    out = {
+        "metric": "output-head int4 GEMV achieved HBM GB/s (150,144 x 2,048, batch 1)",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(med * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4xbf16->fp32", "data": "synthetic (seeded int4 weights, bf16 scales, N(0,1) tokens)",
+        "config": {"workload": "output head 150,144 x 2,048 int4 and dense SwiGLU MLP 2,048 -> 6,144 -> 2,048, "
+                               "decode", "head_bytes": head_bytes, "dense_mlp_bytes": dense_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "k_rows_k2048 (head, one launch)"},
+        "head_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_head.items()},
+        "dense_mlp_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_dense.items()},
+        "dense_mlp_gbps_batch1": round(dense_bytes / res_dense[1][0] / 1e9, 1),
+        "timing_note": "median, p10, p90 of hip-event launch durations; the head and MLP weights rotate over "
+                       "3 and 16 copies so the working set exceeds the last-level cache",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(seconds_budget=20.0):
     """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
     many of the 47 layers as fit the budget; scaled to tokens/s for the whole
@@ -328,6 +398,8 @@ def main():
     ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill path instead: one layer, a 2048-token chunk")
+    ap.add_argument("--head-dense", action="store_true",
+                    help="time the output head and the dense MLP int4 GEMVs instead (batch 1, 4, 16)")
     ap.add_argument("--cost-table", action="store_true",
                     help="time one 47-layer call for n = 1..16 tokens (verify-block cost table)")
     ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
@@ -340,6 +412,9 @@ def main():
         return
     if args.cost_table:
         bench_cost_table(args)
+        return
+    if args.head_dense:
+        bench_head_dense(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

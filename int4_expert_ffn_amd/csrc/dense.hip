@@ -31,9 +31,41 @@ __device__ __forceinline__ void dense_inputs(const float* __restrict__ x, int n,
   wg_sync();
 }
 
-// Wave w of the grid takes rows w, w + waves, ...; U rows per batch, two
-// batches in flight (loads are never conditional, so waiting for one batch
-// never waits for the next: rows past the wave's last one re-read it).
+// The 8 nibbles of one code dword as bf16 pairs 128 + n' (n' = code + 8), in
+// the pair order of the block input: (k0,k2), (k4,k6), (k1,k3), (k5,k7).
+__device__ __forceinline__ void expand8(uint32_t code, uint32_t* p) {
+  const uint32_t x = code ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const uint32_t K43 = 0x43434343u;
+  p[0] = __builtin_amdgcn_perm(K43, lo, 0x04010400u);
+  p[1] = __builtin_amdgcn_perm(K43, lo, 0x04030402u);
+  p[2] = __builtin_amdgcn_perm(K43, hi, 0x04010400u);
+  p[3] = __builtin_amdgcn_perm(K43, hi, 0x04030402u);
+}
+
+// Lane part of one K = 2048 row for one token from expanded codes: the 32
+// products summed in fp32 in a fixed order, minus 136 * (sum of the lane's
+// activations), times the row's scale.
+__device__ __forceinline__ float lane_dot_expanded(const uint32_t (&p)[16], const uint4 (&a)[4], float asum,
+                                                   float scale) {
+  float acc = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t av[4] = {a[d].x, a[d].y, a[d].z, a[d].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p[4 * d + q]),
+                                            __builtin_bit_cast(bf16x2_t, av[q]), acc, false);
+  }
+  return fmaf(-136.f, asum, acc) * scale;
+}
+
+// Wave w of the grid takes rows w, w + waves, ...; U rows per batch and three
+// batches in a ring, two in flight while one is used (loads are never
+// conditional, so waiting for one batch never waits for a younger one: rows
+// past the wave's last one re-read it).  The first two batches are requested
+// before the block inputs are computed.  Each row's codes are expanded once
+// and used for every token.
 // SWIGLU: y[t][r] = silu(W0[r] . a_t) * (W1[r] . a_t), else y[t][r] = W0[r] . a_t.
 template <bool SWIGLU, int U>
 __global__ void __launch_bounds__(NT, 2) k_rows_k2048(const float* __restrict__ x, int n,
@@ -41,13 +73,11 @@ __global__ void __launch_bounds__(NT, 2) k_rows_k2048(const float* __restrict__ 
                                                       const uint8_t* __restrict__ c1, const uint16_t* __restrict__ s1,
                                                       int rows, float* __restrict__ y) {
   __shared__ DenseInput in;
-  dense_inputs(x, n, in);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gw = blockIdx.x * NWAVES + wave, nw = gridDim.x * NWAVES;
-  if (gw >= rows) return;   // no barrier follows
-  const int my_rows = (rows - 1 - gw) / nw + 1;
-  const int nb = (my_rows + U - 1) / U;
-  auto row_of = [&](int j) { return (size_t)gw + (size_t)min(j, my_rows - 1) * nw; };
+  const int my_rows = gw < rows ? (rows - 1 - gw) / nw + 1 : 1;   // waves past the last row re-read row 0..
+  const int nb = gw < rows ? (my_rows + U - 1) / U : 0;
+  auto row_of = [&](int j) { return (size_t)min(gw, rows - 1) + (size_t)min(j, my_rows - 1) * nw; };
   auto load = [&](int b, uint4 (&c)[U], uint32_t (&sc)[U], uint4 (&cu)[U], uint32_t (&su)[U]) {
 #pragma unroll
     for (int i = 0; i < U; ++i) {
@@ -67,24 +97,40 @@ __global__ void __launch_bounds__(NT, 2) k_rows_k2048(const float* __restrict__ 
       const int j = b * U + i;
       if (j >= my_rows) break;   // wave-uniform
       const size_t r = row_of(j);
+      uint32_t pg[16], pu[16];
+      expand8(c[i].x, pg);
+      expand8(c[i].y, pg + 4);
+      expand8(c[i].z, pg + 8);
+      expand8(c[i].w, pg + 12);
+      if (SWIGLU) {
+        expand8(cu[i].x, pu);
+        expand8(cu[i].y, pu + 4);
+        expand8(cu[i].z, pu + 8);
+        expand8(cu[i].w, pu + 12);
+      }
+      const float sg = bf16_bits_to_f32(sc[i]), su_f = SWIGLU ? bf16_bits_to_f32(su[i]) : 0.f;
       for (int t = 0; t < n; ++t) {
         const uint4* at = reinterpret_cast<const uint4*>(in.a[t]);
         const uint4 av[4] = {at[lane], at[64 + lane], at[128 + lane], at[192 + lane]};
         const float asum = in.asum[t][lane];
-        float v = wave_sum(lane_dot_gateup(c[i], av, asum, bf16_bits_to_f32(sc[i])));
-        if (SWIGLU) v = silu_mul(v, wave_sum(lane_dot_gateup(cu[i], av, asum, bf16_bits_to_f32(su[i]))));
+        float v = wave_sum(lane_dot_expanded(pg, av, asum, sg));
+        if (SWIGLU) v = silu_mul(v, wave_sum(lane_dot_expanded(pu, av, asum, su_f)));
         if (lane == 0) y[(size_t)t * rows + r] = v;
       }
     }
   };
-  uint4 ca[U], cb[U], ua[U], ub[U];
-  uint32_t sa[U], sb[U], ta[U], tb[U];
+  uint4 ca[U], cb[U], cc[U], ua[U], ub[U], uc[U];
+  uint32_t sa[U], sb[U], sc_[U], ta[U], tb[U], tc[U];
   load(0, ca, sa, ua, ta);
-  for (int b = 0; b < nb; b += 2) {
-    load(b + 1, cb, sb, ub, tb);
+  load(1, cb, sb, ub, tb);
+  dense_inputs(x, n, in);   // the only barrier; every wave gets here
+  for (int b = 0; b < nb; b += 3) {
+    load(b + 2, cc, sc_, uc, tc);
     compute(b, ca, sa, ua, ta);
-    load(b + 2, ca, sa, ua, ta);
+    load(b + 3, ca, sa, ua, ta);
     compute(b + 1, cb, sb, ub, tb);
+    load(b + 4, cb, sb, ub, tb);
+    compute(b + 2, cc, sc_, uc, tc);
   }
 }
 
@@ -187,7 +233,7 @@ hipError_t launch_head(const uint8_t* codes, const uint16_t* scales, int rows, c
                        hipStream_t s) {
   if (n < 1 || n > DENSE_MAX_TOKENS || rows < 1) return hipErrorInvalidValue;
   const int grid = std::min(DN_GRID, (rows + NWAVES - 1) / NWAVES);
-  hipLaunchKernelGGL((k_rows_k2048<false, 8>), dim3(grid), dim3(NT), 0, s, x, n, codes, scales, codes, scales, rows,
+  hipLaunchKernelGGL((k_rows_k2048<false, 4>), dim3(grid), dim3(NT), 0, s, x, n, codes, scales, codes, scales, rows,
                      logits);
   return hipGetLastError();
 }
