@@ -342,7 +342,7 @@ def bench_head_dense(args):
                                "decode", "head_bytes": head_bytes, "dense_mlp_bytes": dense_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "k_rows_k2048 (head, one launch)"},
+                     "kernel": "k_rows_mfma (head, one launch)"},
         "head_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_head.items()},
         "dense_mlp_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_dense.items()},
         "dense_mlp_gbps_batch1": round(dense_bytes / res_dense[1][0] / 1e9, 1),

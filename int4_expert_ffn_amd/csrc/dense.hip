@@ -134,6 +134,159 @@ __global__ void __launch_bounds__(NT, 2) k_rows_k2048(const float* __restrict__ 
   }
 }
 
+typedef __bf16 dn_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float dn_f32x4 __attribute__((ext_vector_type(4)));
+
+// D = A B + C for 16 x 32 (A) by 32 x 16 (B): lane l holds row l % 16 of A and
+// column l % 16 of B, each for k = 8 (l / 16) .. + 7; D register r of lane l
+// is row 4 (l / 16) + r, column l % 16.
+__device__ __forceinline__ dn_f32x4 mfma16(uint4 a, uint4 b, dn_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dn_bf16x8, a), __builtin_bit_cast(dn_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 expand8_u4(uint32_t code) {
+  uint32_t p[4];
+  expand8(code, p);
+  return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// The tokens' block inputs for the matrix cores: chunk c (8 bf16, pair order)
+// of token t at at[c][t], zero for the tokens past n (16 consecutive 16-byte
+// slots per chunk: one MFMA operand read has no bank conflicts).
+struct DenseTokens {
+  uint4 at[H / 8][DENSE_MAX_TOKENS];
+};
+
+// Rows of K = 2048 on the matrix cores, all tokens of the call at once (the M
+// dimension of v_mfma_f32_16x16x32_bf16 is the 16 tokens, N is 16 weight
+// rows).  Wave w of the grid takes 16-row blocks w, w + waves, ...  Lane l
+// covers weight row l % 16 and, in each 128-element K-group, the 32 elements
+// 32 (l / 16) .. + 31 (16 code bytes): MFMA step s takes their 8-element
+// chunk s.  Each K-group is accumulated from zero as sum (code + 136) a and
+// added times the row's scale; one more MFMA step subtracts
+// 136 sum_g s[r][g] R[t][g], R the sum of a_t over group g split into three
+// bf16 parts (exact products).  A block streams as two chunks of 8 K-groups,
+// the next chunk in flight while one is used.
+// SWIGLU: y[t][r] = silu(W0[r] . a_t) * (W1[r] . a_t), else y[t][r] = W0[r] . a_t.
+// The head runs here; the dense MLP's gate/up run in k_rows_k2048 (6,144 rows
+// make only 384 blocks of 16, too few to fill the chip).
+template <bool SWIGLU>
+__global__ void __launch_bounds__(NT, 2) k_rows_mfma(const float* __restrict__ x, int n,
+                                                     const uint8_t* __restrict__ c0, const uint16_t* __restrict__ s0,
+                                                     const uint8_t* __restrict__ c1, const uint16_t* __restrict__ s1,
+                                                     int rows, float* __restrict__ y) {
+  constexpr int NM = SWIGLU ? 2 : 1;     // matrices
+  constexpr int CG = SWIGLU ? 4 : 8;     // K-groups per streamed chunk
+  constexpr int NCH = 16 / CG;           // chunks per matrix of a block
+  __shared__ DenseInput in;
+  __shared__ DenseTokens tk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, q = lane >> 4;
+  const int gw = blockIdx.x * NWAVES + wave, nw = gridDim.x * NWAVES;
+  const int nblk = (rows + 15) >> 4;
+  const int my_blocks = gw < nblk ? (nblk - 1 - gw) / nw + 1 : 0;
+  const uint8_t* const C[2] = {c0, c1};
+  const uint16_t* const S[2] = {s0, s1};
+  // this lane's weight row in block j of the wave; blocks past the last re-read it
+  auto row_of = [&](int j) {
+    const int b = gw + min(j, max(my_blocks - 1, 0)) * nw;
+    return (size_t)min(b * 16 + col, rows - 1);
+  };
+  // chunk k of a block: K-groups CG h .. CG h + CG - 1 (h = k % NCH) of matrix
+  // k / NCH, and the row's scales of the 8 groups that hold them
+  auto load = [&](int j, int k, uint4 (&c)[CG], uint4& sc) {
+    const size_t r = row_of(j);
+    const int m = k / NCH, h = k % NCH;
+    const uint4* p = reinterpret_cast<const uint4*>(C[m] + r * (H / 2));
+#pragma unroll
+    for (int g = 0; g < CG; ++g) c[g] = p[(CG * h + g) * 4 + q];
+    sc = reinterpret_cast<const uint4*>(S[m] + r * (H / G))[(CG * h) >> 3];
+  };
+  dense_inputs(x, n, in);
+  uint4 ca[CG], cb[CG], sa, sb;
+  load(0, 0, ca, sa);
+  load(0, 1, cb, sb);
+  // transpose the block inputs to at[c][t] (zeros past n)
+  for (int i = threadIdx.x; i < (H / 8) * DENSE_MAX_TOKENS; i += NT) {
+    const int c = i >> 4, t = i & 15;
+    tk.at[c][t] = t < n ? reinterpret_cast<const uint4*>(in.a[t])[(c & 3) * 64 + (c >> 2)] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  wg_sync();   // the only other barrier; every wave gets here
+  // R[t][g] of this lane's token t = l % 16 and groups 8 q + i (q < 2), in three bf16 parts
+  uint4 rp[3];
+  {
+    uint32_t w3[3][4] = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * q + i;
+      float v = 0.f;
+      if (q < 2 && col < n)
+        v = ((in.asum[col][4 * g] + in.asum[col][4 * g + 1]) + in.asum[col][4 * g + 2]) + in.asum[col][4 * g + 3];
+      const uint32_t b0 = f32_to_bf16_rne(v);
+      const float r1 = v - bf16_bits_to_f32(b0);
+      const uint32_t b1 = f32_to_bf16_rne(r1);
+      const uint32_t b2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1));
+      const int sh = 16 * (i & 1);
+      w3[0][i >> 1] |= b0 << sh;
+      w3[1][i >> 1] |= b1 << sh;
+      w3[2][i >> 1] |= b2 << sh;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) rp[k] = make_uint4(w3[k][0], w3[k][1], w3[k][2], w3[k][3]);
+  }
+  auto chunk = [&](int h, const uint4 (&c)[CG], const uint4& sc, dn_f32x4& acc) {
+#pragma unroll
+    for (int g = 0; g < CG; ++g) {
+      const int gg = CG * h + g;   // K-group
+      uint4 a[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) a[st] = tk.at[gg * 16 + 4 * q + st][col];
+      const uint32_t cw[4] = {c[g].x, c[g].y, c[g].z, c[g].w};
+      dn_f32x4 temp = mfma16(a[0], expand8_u4(cw[0]), dn_f32x4{});
+#pragma unroll
+      for (int st = 1; st < 4; ++st) temp = mfma16(a[st], expand8_u4(cw[st]), temp);
+      const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+      const int gi = gg & 7;
+      const float sg = bf16_bits_to_f32((gi & 1) ? (sw[gi >> 1] >> 16) : (sw[gi >> 1] & 0xFFFFu));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = gg == 0 ? sg * temp[r] : fmaf(sg, temp[r], acc[r]);
+      __builtin_amdgcn_sched_barrier(0);   // one K-group at a time: bounded register use
+    }
+  };
+  // NM x NCH chunks per block through two buffers; the chunk two ahead
+  // (possibly of the next block) is requested as soon as a buffer is free
+  constexpr int NK = NM * NCH;
+  for (int j = 0; j < my_blocks; ++j) {
+    dn_f32x4 acc[NM];
+    uint4 shalf[NM][2];   // scales of groups 0..7 and 8..15, for the correction
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      uint4(&c)[CG] = (k & 1) ? cb : ca;
+      uint4& sc = (k & 1) ? sb : sa;
+      chunk(k % NCH, c, sc, acc[k / NCH]);
+      shalf[k / NCH][(CG * (k % NCH)) >> 3] = sc;
+      const int kn = k + 2;
+      load(kn < NK ? j : j + 1, kn % NK, c, sc);
+    }
+    float v[NM][4];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint4 bs = q == 0 ? shalf[m][0] : q == 1 ? shalf[m][1] : make_uint4(0u, 0u, 0u, 0u);
+      dn_f32x4 corr = mfma16(rp[0], bs, dn_f32x4{});
+      corr = mfma16(rp[1], bs, corr);
+      corr = mfma16(rp[2], bs, corr);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[m][r] = fmaf(-136.f, corr[r], acc[m][r]);
+    }
+    const int row = (gw + j * nw) * 16 + col;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * q + r;
+      if (t < n && row < rows) y[(size_t)t * rows + row] = SWIGLU ? silu_mul(v[0][r], v[NM - 1][r]) : v[0][r];
+    }
+  }
+}
+
 // ------------------------------------------------------------- dense down
 // out[t][c] = x[t][c] + Wd[c] . h_t, K = inter = P x 2048.  Wave w of
 // workgroup b owns rows 16 b + 4 w .. + 3; lane L covers k = 2048 p + 32 L ..
@@ -216,7 +369,7 @@ __global__ void __launch_bounds__(DD_NT) k_dense_down(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------- host side
-constexpr int DN_GRID = 256;   // one workgroup per CU: 8 waves, 16 rows in flight each
+constexpr int DN_GRID = 256;   // one workgroup per CU (132 KB of LDS)
 
 hipError_t launch_dense_mlp(const uint8_t* gate, const uint16_t* gate_s, const uint8_t* up, const uint16_t* up_s,
                             const uint8_t* down, const uint16_t* down_s, int inter, const float* x, int n, float* h,
@@ -232,8 +385,8 @@ hipError_t launch_dense_mlp(const uint8_t* gate, const uint16_t* gate_s, const u
 hipError_t launch_head(const uint8_t* codes, const uint16_t* scales, int rows, const float* x, int n, float* logits,
                        hipStream_t s) {
   if (n < 1 || n > DENSE_MAX_TOKENS || rows < 1) return hipErrorInvalidValue;
-  const int grid = std::min(DN_GRID, (rows + NWAVES - 1) / NWAVES);
-  hipLaunchKernelGGL((k_rows_k2048<false, 4>), dim3(grid), dim3(NT), 0, s, x, n, codes, scales, codes, scales, rows,
+  const int grid = std::min(DN_GRID, ((rows + 15) / 16 + NWAVES - 1) / NWAVES);
+  hipLaunchKernelGGL(k_rows_mfma<false>, dim3(grid), dim3(NT), 0, s, x, n, codes, scales, codes, scales, rows,
                      logits);
   return hipGetLastError();
 }

@@ -311,7 +311,7 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 static int check_q4(flint_q4 m, const char* name) {
   if (!m.codes || !m.scales) return fail(FLINT_ERR_INVALID_ARG, "%s: codes or scales is NULL", name);
   if (misaligned16(m.codes)) return fail(FLINT_ERR_INVALID_ARG, "%s: codes must be 16-byte aligned", name);
-  if ((uintptr_t)m.scales & 1) return fail(FLINT_ERR_INVALID_ARG, "%s: scales must be 2-byte aligned", name);
+  if (misaligned16(m.scales)) return fail(FLINT_ERR_INVALID_ARG, "%s: scales must be 16-byte aligned", name);
   return FLINT_OK;
 }
 

@@ -79,7 +79,7 @@ def test_dense_and_head_reject_bad_arguments_before_any_hip_call():
     # dense MLP
     assert lib.flint_dense_mlp_forward(F.q4(None, A), good, good, W, x, 1, h, out, None) == inval
     assert lib.flint_dense_mlp_forward(F.q4(A + 8, A), good, good, W, x, 1, h, out, None) == inval
-    assert lib.flint_dense_mlp_forward(F.q4(A, A + 1), good, good, W, x, 1, h, out, None) == inval
+    assert lib.flint_dense_mlp_forward(F.q4(A, A + 2), good, good, W, x, 1, h, out, None) == inval
     assert lib.flint_dense_mlp_forward(good, good, good, W, None, 1, h, out, None) == inval
     assert lib.flint_dense_mlp_forward(good, good, good, W, x + 4, 1, h, out, None) == inval
     for n in (0, F.FLINT_DENSE_MAX_TOKENS + 1):
