@@ -54,13 +54,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack47_traffic.txt")
 DECODE_KERNEL = "k_decode_persistent"
 
 
-def traffic_from_profiles():
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel sources; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_from_profiles(path=None):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    summary (the decode kernel by default), if it was taken on the current
+    kernel sources; else None."""
+    path = path or TRAFFIC_FILE
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -88,10 +90,22 @@ def _counter_values(run_dir, counter, name_pattern=None):
     return out
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
-    """Write the traffic summary from four rocprofv3 --pmc runs: the decode
-    benchmark (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) and a plain 1 GiB
-    device copy (the same two counters) that calibrates them."""
+HEAD_KERNEL = "k_rows_mfma"
+HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_kernel_traffic.txt")
+HEAD_BYTES = 150144 * (H // 2) + 150144 * (H // G) * 2                # 158,552,064
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands, which="decode"):
+    """Write the traffic summary from four rocprofv3 --pmc runs: the benchmark
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch of its dominant kernel) and a
+    plain 1 GiB device copy (the same two counters) that calibrates them.
+    which: "decode" (47-layer decode launch) or "head" (output head launch)."""
+    kernel, out_file, algo, title = {
+        "decode": (DECODE_KERNEL, TRAFFIC_FILE, TOKEN_BYTES,
+                   "# HBM traffic of one decode launch (47-layer Flint MoE stack, batch 1, the bench workload)"),
+        "head": (HEAD_KERNEL, HEAD_TRAFFIC_FILE, HEAD_BYTES,
+                 "# HBM traffic of one output-head launch (150,144 x 2,048 int4, bench.py --head-dense workload)"),
+    }[which]
     def one(d, counter, pattern):
         vals = _counter_values(d, counter, pattern)
         if not vals:
@@ -99,8 +113,8 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
         name = max(vals, key=lambda k: len(vals[k]))
         return name, vals[name]
     copy_bytes = 1 << 30
-    kname, f = one(fetch_dir, "FETCH_SIZE", DECODE_KERNEL)
-    _, w = one(write_dir, "WRITE_SIZE", DECODE_KERNEL)
+    kname, f = one(fetch_dir, "FETCH_SIZE", kernel)
+    _, w = one(write_dir, "WRITE_SIZE", kernel)
     cf = max(max(v) for v in _counter_values(copy_fetch_dir, "FETCH_SIZE").values())
     cw_all = _counter_values(copy_write_dir, "WRITE_SIZE")
     cw = max(max(v) for v in cw_all.values())
@@ -109,7 +123,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
     f_kib, w_kib = float(np.median(f)), float(np.median(w))
     total = f_kib * 1024.0 * f_factor + w_kib * 1024.0 * w_factor
     lines = [
-        "# HBM traffic of one decode launch (47-layer Flint MoE stack, batch 1, the bench workload)",
+        title,
         "# from rocprofv3 --pmc, one counter per run, calibrated with a plain 1 GiB device copy",
         f"kernel: {kname}",
         f"kernel_source_hash: {kernel_source_hash()}",
@@ -121,11 +135,11 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
         f"fetch_factor: {f_factor:.4f}",
         f"write_factor: {w_factor:.4f}",
         f"hbm_bytes_per_launch: {int(round(total))}",
-        f"algorithmic_bytes_per_launch: {TOKEN_BYTES}",
-        f"traffic_over_algorithmic: {total / TOKEN_BYTES:.3f}",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"traffic_over_algorithmic: {total / algo:.3f}",
     ] + [f"command: {c}" for c in commands]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    os.makedirs(os.path.dirname(out_file), exist_ok=True)
+    with open(out_file, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -191,6 +205,8 @@ def bench_prefill(args):
                      "layer_us_median": round(layer_s * 1e6, 2),
                      "weight_and_activation_gbps": round((weight_bytes + act_bytes) / layer_s / 1e9, 1)},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
@@ -341,7 +357,7 @@ def bench_head_dense(args):
         "config": {"workload": "output head 150,144 x 2,048 int4 and dense SwiGLU MLP 2,048 -> 6,144 -> 2,048, "
                                "decode", "head_bytes": head_bytes, "dense_mlp_bytes": dense_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profiles(HEAD_TRAFFIC_FILE),
                      "kernel": "k_rows_mfma (head, one launch)"},
         "head_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_head.items()},
         "dense_mlp_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_dense.items()},
@@ -349,7 +365,61 @@ def bench_head_dense(args):
         "timing_note": "median, p10, p90 of hip-event launch durations; the head and MLP weights rotate over "
                        "3 and 16 copies so the working set exceeds the last-level cache",
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_head(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _oracle_threads():
+    try:
+        import threadpoolctl
+        return int(max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1))
+    except Exception:
+        return 1
+
+
+def cpu_baseline_prefill(seconds_budget=20.0):
+    """The CPU oracle on a bounded sample of the prefill workload: tokens of the
+    2,048-token Zipf chunk through the layer, one at a time (the oracle has no
+    batched path), scaled to tokens/s through one layer."""
+    import flintgen as fg
+    from oracle import flint_oracle as O
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_sources import SynthSource
+    synth = fg.Synth(fg.FLINT, seed=0, n_layers=1, bias_kind="zipf")
+    src = SynthSource(synth)
+    t0 = time.perf_counter()
+    done = 0
+    for t in range(PF_TOKENS):
+        x = fg.token(0, 2000 + t)
+        O.moe_block(O.block_input(x, fg.FLINT), src, 0, fg.FLINT)
+        done += 1
+        if time.perf_counter() - t0 > seconds_budget:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 4), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"the first {done} tokens of the 2,048-token chunk through layer 0 ({dt:.1f} s, weights "
+                      f"regenerated per token included)"}
+
+
+def cpu_baseline_head(seconds_budget=20.0):
+    """The CPU oracle on a bounded sample of the head: logits of one token for
+    blocks of 4,096 rows, timing the oracle call only; scaled to GB/s of int4
+    weights processed."""
+    import flintgen as fg
+    from oracle import flint_oracle as O
+    x = fg.token(0, 40)
+    spent, rows = 0.0, 0
+    while spent < seconds_budget and rows < fg.VOCAB:
+        r1 = min(rows + 4096, fg.VOCAB)
+        c, sc = fg.head(0, row_ids=range(rows, r1))
+        t0 = time.perf_counter()
+        O.head_logits(x, c.numpy(), sc.numpy(), fg.FLINT)
+        spent += time.perf_counter() - t0
+        rows = r1
+    gbps = rows * (H // 2 + (H // G) * 2) / spent / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"one token, head rows 0..{rows - 1} in blocks of 4,096 ({spent:.1f} s of oracle time)"}
 
 
 def cpu_baseline(seconds_budget=20.0):
@@ -396,6 +466,8 @@ def main():
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the traffic summary under profiles/ from four rocprofv3 --pmc output folders")
     ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
+    ap.add_argument("--counters-kernel", choices=("decode", "head"), default="decode",
+                    help="which kernel --counters-summary summarises")
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill path instead: one layer, a 2048-token chunk")
     ap.add_argument("--head-dense", action="store_true",
@@ -405,7 +477,7 @@ def main():
     ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
     args = ap.parse_args()
     if args.counters_summary:
-        summarize_counters(*args.counters_summary, commands=args.command)
+        summarize_counters(*args.counters_summary, commands=args.command, which=args.counters_kernel)
         return
     if args.prefill:
         bench_prefill(args)
