@@ -440,6 +440,224 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
 #endif
 }
 
+// ------------------------------------------------------------- token groups
+// Persistent decode for 2..16 tokens: the grid splits into one group of
+// P = NWG / K workgroups per token (K = the next power of two >= n; groups of
+// tokens past n exit at once).  A group runs the single-token schedule above
+// for its token with every workgroup doing K times the rows: router rows
+// K u .. K u + K - 1, shared gate/up rows 4 K u .., routed gate/up rows
+// 12 K u .. of the token's six experts, and output rows 8 K u ...  Its
+// exchanges carry one token and involve only its P workgroups, so their size
+// does not grow with n.  Every row is computed by the same device function
+// with the same reduction shape as in a single-token call, so each token's
+// result is bitwise the same as running it alone.
+template <int K>
+__global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
+  constexpr int P = NWG / K;
+  constexpr int NSH = 4 * K, NRT = 12 * K, NTASK = NSH + NRT;   // gate/up row pairs of a workgroup
+  constexpr int NOUT = 8 * K;                                     // output rows of a workgroup
+  __shared__ __align__(16) uint4 a_lds[256];
+  __shared__ float asum_lds[64];
+  __shared__ float xown[NOUT];
+  __shared__ __align__(16) uint32_t stage[HW];   // gather destination: x, then (c, s), then h
+  float* const xstage = reinterpret_cast<float*>(stage);
+  float* const hbuf = reinterpret_cast<float*>(stage);
+  __shared__ float hloc[NTASK];
+  __shared__ int hloc_idx[NTASK];
+  __shared__ int n_hloc;
+  __shared__ float xnew[NOUT];
+  __shared__ int ids_l[TOPK];
+  __shared__ float w_l[TOPK];
+  __shared__ double red[2][NWAVES];
+  __shared__ double zpart[K][NWAVES];
+  __shared__ int bail[2];
+  GtsLds gts_lds = nullptr;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t = blockIdx.x / P, u = blockIdx.x % P;   // token of this group, workgroup in the group
+  if (t >= A.n) return;                               // no group waits for this workgroup
+  const bool poller = wave != PUB_WAVE;
+
+  if (tid < 2) bail[tid] = 0;
+  int bail_par = 0;
+  auto sync_or = [&](bool fail) {
+    if (fail) bail[bail_par] = 1;
+    wg_sync();
+    const bool r = bail[bail_par] != 0;
+    bail_par ^= 1;
+    return r;
+  };
+  wg_sync();
+
+  for (int l = A.l0; l < A.l1; ++l) {
+    const LayerW L = layer_at(A.base, A.layer_stride, l);
+    const uint32_t tag = A.epoch + ((uint32_t)l << 2);
+    // router rows of this workgroup: requested before the x exchange
+    uint2 rw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) rw[j] = load_router_part(L.router + (size_t)(K * u + j) * H);
+
+    // ---------------- P0: block input
+    bool ok = true;
+    if (l == A.l0) {
+      if (tid < H / 4) reinterpret_cast<float4*>(xstage)[tid] = reinterpret_cast<const float4*>(A.x + (size_t)t * H)[tid];
+    } else if (poller) {
+      ok = gather<(H + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xx + (size_t)t * H, H, tag - 4 + 2,
+                                                          reinterpret_cast<uint32_t*>(xstage), A.err, Identity(), tid,
+                                                          l, -1, gts_lds);
+    }
+    if (sync_or(!ok)) return;
+    const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
+    if (tid >= (NOUT / 4) * u && tid < (NOUT / 4) * (u + 1)) {   // this workgroup's output rows, kept for the residual
+      float* xo = xown + 4 * (tid - (NOUT / 4) * u);
+      xo[0] = xv.x; xo[1] = xv.y; xo[2] = xv.z; xo[3] = xv.w;
+    }
+    block_input(xv, reinterpret_cast<uint32_t*>(a_lds), asum_lds, red[l & 1]);
+    wg_sync();
+
+    // ---------------- P1: router rows -> the publisher wave writes (c, s)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const double p = router_part(rw[j], a_lds);
+      if (lane == 0) zpart[j][wave] = p;
+    }
+    wg_sync();
+    if (wave == PUB_WAVE && lane < K) {
+      const int e = K * u + lane;
+      double sv, cv;
+      router_scores(zpart[lane], L.bias[e], sv, cv);
+      const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
+      const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
+      uint64_t* z = A.xz + (size_t)t * 4 * E;
+      publish(z + 2 * e, tag, (uint32_t)cb);
+      publish(z + 2 * e + 1, tag, (uint32_t)(cb >> 32));
+      publish(z + 2 * E + 2 * e, tag, (uint32_t)sb);
+      publish(z + 2 * E + 2 * e + 1, tag, (uint32_t)(sb >> 32));
+    }
+
+    // ---------------- P2: routing, gate/up
+    ok = true;
+    if (poller)
+      ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
+                                                                Identity(), tid, l, -1, gts_lds);
+    if (sync_or(!ok)) return;
+    if (wave == 0) {
+      const double* zc = reinterpret_cast<const double*>(stage);
+      route_token(zc, zc + E, ids_l, w_l);
+    }
+    if (tid == 0) n_hloc = 0;
+    wg_sync();
+    if (u == 0 && A.trace_ids && wave == PUB_WAVE && lane < TOPK) {
+      const size_t o = ((size_t)l * A.trace_cap + t) * TOPK + lane;
+      A.trace_ids[o] = ids_l[lane];
+      A.trace_w[o] = w_l[lane];
+    }
+    // down codes of this wave's first output row: needed after the h exchange
+    const int row0 = NOUT * u + wave;
+    uint4 ca0, cb0;
+    uint32_t sa0, sb0;
+    load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
+    {
+      // task j: j < NSH shared row NSH u + j, else routed row q = NRT u + j - NSH
+      // of the token's experts in pick order (slot q / I, row q % I); task j
+      // goes to wave j % 8, TB tasks in flight per wave
+      constexpr int TB = 2;
+      uint4 qg[TB], qu[TB];
+      uint32_t qsg[TB], qsu[TB];
+      auto task_row = [&](int j, const uint8_t*& g, const uint16_t*& gs, const uint8_t*& up, const uint16_t*& us,
+                          size_t& rr) {
+        if (j < NSH) {
+          rr = (size_t)NSH * u + j;
+          g = L.sh_gate; gs = L.sh_gate_s; up = L.sh_up; us = L.sh_up_s;
+        } else {
+          const int q = NRT * u + (j - NSH);
+          rr = (size_t)ids_l[q / I] * I + (q % I);
+          g = L.gate; gs = L.gate_s; up = L.up; us = L.up_s;
+        }
+      };
+      auto load_batch = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const int j = j0 + b * NWAVES;
+          if (j < NTASK) {
+            const uint8_t *g, *up;
+            const uint16_t *gs, *us;
+            size_t rr;
+            task_row(j, g, gs, up, us, rr);
+            qg[b] = reinterpret_cast<const uint4*>(g + rr * (H / 2))[lane];
+            qu[b] = reinterpret_cast<const uint4*>(up + rr * (H / 2))[lane];
+            qsg[b] = gs[rr * (H / G) + (lane >> 2)];
+            qsu[b] = us[rr * (H / G) + (lane >> 2)];
+          }
+        }
+      };
+      auto compute_batch = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const int j = j0 + b * NWAVES;
+          if (j >= NTASK) break;
+          const int word = j < NSH ? TOPK * I + NSH * u + j : NRT * u + (j - NSH);   // slot * I + row
+          const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
+          if (lane == 0) {
+            const int k = atomicAdd(&n_hloc, 1);   // < NTASK: one value per task
+            hloc[k] = hv;
+            hloc_idx[k] = word;
+          }
+        }
+      };
+      for (int j0 = wave; j0 < NTASK; j0 += TB * NWAVES) {
+        load_batch(j0);
+        compute_batch(j0);
+      }
+    }
+    wg_sync();
+    if (wave == PUB_WAVE) {
+      const int cnt = n_hloc;
+      for (int k = lane; k < cnt; k += 64) {
+        const int word = hloc_idx[k];
+        if (word >= 0 && word < HW) publish(A.xh + (size_t)t * HW + word, tag + 1, __float_as_uint(hloc[k]));
+        else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+
+    // ---------------- P3: output rows NOUT u + wave + 8 i (i < K), fixed-order combine
+    ok = true;
+    if (poller)
+      ok = gather<(HW + NPOLL - 1) / NPOLL, HPos, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
+                                                        reinterpret_cast<uint32_t*>(hbuf), A.err, HPos(), tid, l, -1,
+                                                        gts_lds);
+    if (sync_or(!ok)) return;
+    {
+      const int sub = lane & 15;
+      auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
+      auto load_b = [&] {
+        return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
+                           : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
+      };
+      uint4 ca = ca0, cb = cb0;
+      uint32_t sa = sa0, sb = sb0;
+      for (int i = 0; i < K; ++i) {
+        const int lr = wave + NWAVES * i;   // local output row
+        uint4 nca = ca, ncb = cb;
+        uint32_t nsa = sa, nsb = sb;
+        if (i + 1 < K) load_down_row(L, ids_l, NOUT * u + lr + NWAVES, nca, nsa, ncb, nsb);
+        const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
+        if (lane == 0) xnew[lr] = v;
+        ca = nca; cb = ncb; sa = nsa; sb = nsb;
+      }
+    }
+    wg_sync();
+    if (wave == PUB_WAVE) {
+      for (int i = lane; i < NOUT; i += 64) {
+        const int r = NOUT * u + i;
+        const float v = xnew[i];
+        if (l + 1 < A.l1) publish(A.xx + (size_t)t * H + r, tag + 2, __float_as_uint(v));
+        else A.out[(size_t)t * H + r] = v;
+      }
+    }
+  }
+}
+
 __global__ void k_clear_words(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
@@ -447,8 +665,12 @@ __global__ void k_clear_words(uint64_t* p, size_t n) {
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   PersistArgs a = args;
   void* kargs[] = {&a};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_decode_persistent), dim3(NWG), dim3(NT), kargs,
-                                    0, s);
+  const void* k = reinterpret_cast<const void*>(k_decode_persistent);
+  if (a.n > 8) k = reinterpret_cast<const void*>(k_decode_groups<16>);
+  else if (a.n > 4) k = reinterpret_cast<const void*>(k_decode_groups<8>);
+  else if (a.n > 2) k = reinterpret_cast<const void*>(k_decode_groups<4>);
+  else if (a.n > 1) k = reinterpret_cast<const void*>(k_decode_groups<2>);
+  return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
 }
 
 hipError_t clear_exchange(uint64_t* p, size_t n_words, hipStream_t s) {
