@@ -561,7 +561,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       // task j: j < NSH shared row NSH u + j, else routed row q = NRT u + j - NSH
       // of the token's experts in pick order (slot q / I, row q % I); task j
       // goes to wave j % 8, TB tasks in flight per wave
-      constexpr int TB = 2;
+      constexpr int TB = K >= 4 ? 4 : 2;
       uint4 qg[TB], qu[TB];
       uint32_t qsg[TB], qsu[TB];
       auto task_row = [&](int j, const uint8_t*& g, const uint16_t*& gs, const uint8_t*& up, const uint16_t*& us,
