@@ -441,10 +441,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
 }
 
 // ------------------------------------------------------------- token groups
-// Persistent decode for 2..16 tokens: the grid splits into one group of
-// P = NWG / K workgroups per token (K = the next power of two >= n; groups of
-// tokens past n exit at once).  A group runs the single-token schedule above
-// for its token with every workgroup doing K times the rows: router rows
+// Persistent decode for n = K = 2, 4, 8 or 16 tokens: the grid splits into
+// one group of P = NWG / K workgroups per token.  A group runs the
+// single-token schedule above for its token with every workgroup doing K
+// times the rows: router rows
 // K u .. K u + K - 1, shared gate/up rows 4 K u .., routed gate/up rows
 // 12 K u .. of the token's six experts, and output rows 8 K u ...  Its
 // exchanges carry one token and involve only its P workgroups, so their size
@@ -658,6 +658,225 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
   }
 }
 
+// ------------------------------------------------------------- token groups, any n
+// Persistent decode for token counts that are not powers of two: the grid
+// splits into one group of P = NWG / n workgroups per token (rounded down;
+// the workgroups past n P exit at once).  A group runs the single-token
+// schedule above for its token, with workgroup u of the group taking the u-th
+// of P near-equal ranges of each kind of row: router rows (experts), shared
+// gate/up rows, the token's routed gate/up rows and output rows.  A range
+// holds at most K times the rows of a single-token workgroup, for K the power
+// of two at or above n (then NWG / P <= K).
+// Its exchanges carry one token and involve only its P workgroups, so their
+// size does not grow with n.  Every row is computed by the same device
+// function with the same reduction shape as in a single-token call, so each
+// token's result is bitwise the same as running it alone.
+template <int K>
+__global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
+  constexpr int MSH = 4 * K, MRT = 12 * K, MTASK = MSH + MRT;   // most gate/up row pairs of a workgroup
+  constexpr int MOUT = 8 * K;                                   // most output rows of a workgroup
+  __shared__ __align__(16) uint4 a_lds[256];
+  __shared__ float asum_lds[64];
+  __shared__ float xown[MOUT];
+  __shared__ __align__(16) uint32_t stage[HW];   // gather destination: x, then (c, s), then h
+  float* const xstage = reinterpret_cast<float*>(stage);
+  float* const hbuf = reinterpret_cast<float*>(stage);
+  __shared__ float hloc[MTASK];
+  __shared__ int hloc_idx[MTASK];
+  __shared__ int n_hloc;
+  __shared__ float xnew[MOUT];
+  __shared__ int ids_l[TOPK];
+  __shared__ float w_l[TOPK];
+  __shared__ double red[2][NWAVES];
+  __shared__ double zpart[K][NWAVES];
+  __shared__ int bail[2];
+  GtsLds gts_lds = nullptr;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int P = NWG / A.n;
+  const int t = blockIdx.x / P, u = blockIdx.x % P;   // token of this group, workgroup in the group
+  if (t >= A.n) return;                               // no group waits for this workgroup
+  const bool poller = wave != PUB_WAVE;
+  // this workgroup's ranges: [T u / P, T (u + 1) / P) of T rows
+  auto lo = [&](int T) { return T * u / P; };
+  auto hi = [&](int T) { return T * (u + 1) / P; };
+  const int r0 = lo(E), nr = hi(E) - r0;                       // router rows (experts)
+  const int s0 = lo(IS), nsh = hi(IS) - s0;                    // shared gate/up rows
+  const int q0 = lo(TOPK * I), nrt = hi(TOPK * I) - q0;        // routed gate/up rows of the token
+  const int o0 = lo(H), nout = hi(H) - o0;                     // output rows
+  const int ntask = nsh + nrt;
+
+  if (tid < 2) bail[tid] = 0;
+  int bail_par = 0;
+  auto sync_or = [&](bool fail) {
+    if (fail) bail[bail_par] = 1;
+    wg_sync();
+    const bool r = bail[bail_par] != 0;
+    bail_par ^= 1;
+    return r;
+  };
+  wg_sync();
+
+  for (int l = A.l0; l < A.l1; ++l) {
+    const LayerW L = layer_at(A.base, A.layer_stride, l);
+    const uint32_t tag = A.epoch + ((uint32_t)l << 2);
+    // router rows of this workgroup: requested before the x exchange
+    uint2 rw[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j < nr) rw[j] = load_router_part(L.router + (size_t)(r0 + j) * H);
+
+    // ---------------- P0: block input
+    bool ok = true;
+    if (l == A.l0) {
+      if (tid < H / 4) reinterpret_cast<float4*>(xstage)[tid] = reinterpret_cast<const float4*>(A.x + (size_t)t * H)[tid];
+    } else if (poller) {
+      ok = gather<(H + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xx + (size_t)t * H, H, tag - 4 + 2,
+                                                          reinterpret_cast<uint32_t*>(xstage), A.err, Identity(), tid,
+                                                          l, -1, gts_lds);
+    }
+    if (sync_or(!ok)) return;
+    for (int i = tid; i < nout; i += NT) xown[i] = xstage[o0 + i];   // this workgroup's rows, for the residual
+    const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
+    block_input(xv, reinterpret_cast<uint32_t*>(a_lds), asum_lds, red[l & 1]);
+    wg_sync();
+
+    // ---------------- P1: router rows -> the publisher wave writes (c, s)
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (j < nr) {
+        const double p = router_part(rw[j], a_lds);
+        if (lane == 0) zpart[j][wave] = p;
+      }
+    }
+    wg_sync();
+    if (wave == PUB_WAVE && lane < nr) {
+      const int e = r0 + lane;
+      double sv, cv;
+      router_scores(zpart[lane], L.bias[e], sv, cv);
+      const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
+      const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
+      uint64_t* z = A.xz + (size_t)t * 4 * E;
+      publish(z + 2 * e, tag, (uint32_t)cb);
+      publish(z + 2 * e + 1, tag, (uint32_t)(cb >> 32));
+      publish(z + 2 * E + 2 * e, tag, (uint32_t)sb);
+      publish(z + 2 * E + 2 * e + 1, tag, (uint32_t)(sb >> 32));
+    }
+
+    // ---------------- P2: routing, gate/up
+    ok = true;
+    if (poller)
+      ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
+                                                                Identity(), tid, l, -1, gts_lds);
+    if (sync_or(!ok)) return;
+    if (wave == 0) {
+      const double* zc = reinterpret_cast<const double*>(stage);
+      route_token(zc, zc + E, ids_l, w_l);
+    }
+    if (tid == 0) n_hloc = 0;
+    wg_sync();
+    if (u == 0 && A.trace_ids && wave == PUB_WAVE && lane < TOPK) {
+      const size_t o = ((size_t)l * A.trace_cap + t) * TOPK + lane;
+      A.trace_ids[o] = ids_l[lane];
+      A.trace_w[o] = w_l[lane];
+    }
+    // down codes of this wave's first output row: needed after the h exchange
+    uint4 ca0 = make_uint4(0u, 0u, 0u, 0u), cb0 = ca0;
+    uint32_t sa0 = 0u, sb0 = 0u;
+    if (wave < nout) load_down_row(L, ids_l, o0 + wave, ca0, sa0, cb0, sb0);
+    {
+      // task j: j < nsh shared row s0 + j, else routed row q = q0 + j - nsh of
+      // the token's experts in pick order (slot q / I, row q % I); task j goes
+      // to wave j % 8, TB tasks in flight per wave
+      constexpr int TB = K >= 4 ? 4 : 2;
+      uint4 qg[TB], qu[TB];
+      uint32_t qsg[TB], qsu[TB];
+      auto load_batch = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const int j = j0 + b * NWAVES;
+          if (j < ntask) {
+            const bool sh = j < nsh;
+            const int q = q0 + (j - nsh);
+            const size_t rr = sh ? (size_t)(s0 + j) : (size_t)ids_l[q / I] * I + (q % I);
+            qg[b] = reinterpret_cast<const uint4*>((sh ? L.sh_gate : L.gate) + rr * (H / 2))[lane];
+            qu[b] = reinterpret_cast<const uint4*>((sh ? L.sh_up : L.up) + rr * (H / 2))[lane];
+            qsg[b] = (sh ? L.sh_gate_s : L.gate_s)[rr * (H / G) + (lane >> 2)];
+            qsu[b] = (sh ? L.sh_up_s : L.up_s)[rr * (H / G) + (lane >> 2)];
+          }
+        }
+      };
+      auto compute_batch = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const int j = j0 + b * NWAVES;
+          if (j >= ntask) break;
+          const int word = j < nsh ? TOPK * I + s0 + j : q0 + (j - nsh);   // slot * I + row
+          const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
+          if (lane == 0) {
+            const int k = atomicAdd(&n_hloc, 1);   // < ntask <= MTASK: one value per task
+            hloc[k] = hv;
+            hloc_idx[k] = word;
+          }
+        }
+      };
+      for (int j0 = wave; j0 < ntask; j0 += TB * NWAVES) {
+        load_batch(j0);
+        compute_batch(j0);
+      }
+    }
+    wg_sync();
+    if (wave == PUB_WAVE) {
+      const int cnt = n_hloc;
+      for (int k = lane; k < cnt; k += 64) {
+        const int word = hloc_idx[k];
+        if (word >= 0 && word < HW) publish(A.xh + (size_t)t * HW + word, tag + 1, __float_as_uint(hloc[k]));
+        else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+
+    // ---------------- P3: output rows o0 + wave + 8 i, fixed-order combine
+    ok = true;
+    if (poller)
+      ok = gather<(HW + NPOLL - 1) / NPOLL, HPos, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
+                                                        reinterpret_cast<uint32_t*>(hbuf), A.err, HPos(), tid, l, -1,
+                                                        gts_lds);
+    if (sync_or(!ok)) return;
+    {
+      const int sub = lane & 15;
+      auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
+      auto load_b = [&] {
+        return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
+                           : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
+      };
+      // unrolled with a fixed bound: the prefetched codes are renamed, never
+      // copied (a copy would wait for the load in flight)
+      uint4 ca = ca0, cb = cb0;
+      uint32_t sa = sa0, sb = sb0;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {   // nout <= 8 K
+        const int lr = wave + NWAVES * i;   // local output row
+        if (lr >= nout) break;
+        uint4 nca = ca, ncb = cb;
+        uint32_t nsa = sa, nsb = sb;
+        if (lr + NWAVES < nout) load_down_row(L, ids_l, o0 + lr + NWAVES, nca, nsa, ncb, nsb);
+        const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
+        if (lane == 0) xnew[lr] = v;
+        ca = nca; cb = ncb; sa = nsa; sb = nsb;
+      }
+    }
+    wg_sync();
+    if (wave == PUB_WAVE) {
+      for (int i = lane; i < nout; i += 64) {
+        const int r = o0 + i;
+        const float v = xnew[i];
+        if (l + 1 < A.l1) publish(A.xx + (size_t)t * H + r, tag + 2, __float_as_uint(v));
+        else A.out[(size_t)t * H + r] = v;
+      }
+    }
+  }
+}
+
 __global__ void k_clear_words(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
@@ -665,11 +884,16 @@ __global__ void k_clear_words(uint64_t* p, size_t n) {
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   PersistArgs a = args;
   void* kargs[] = {&a};
+  // one token: the schedule above; 2, 4, 8, 16 tokens: fixed power-of-two
+  // groups (statically sized loops); other counts: exact ranges
   const void* k = reinterpret_cast<const void*>(k_decode_persistent);
-  if (a.n > 8) k = reinterpret_cast<const void*>(k_decode_groups<16>);
-  else if (a.n > 4) k = reinterpret_cast<const void*>(k_decode_groups<8>);
-  else if (a.n > 2) k = reinterpret_cast<const void*>(k_decode_groups<4>);
-  else if (a.n > 1) k = reinterpret_cast<const void*>(k_decode_groups<2>);
+  if (a.n == 2) k = reinterpret_cast<const void*>(k_decode_groups<2>);
+  else if (a.n == 4) k = reinterpret_cast<const void*>(k_decode_groups<4>);
+  else if (a.n == 8) k = reinterpret_cast<const void*>(k_decode_groups<8>);
+  else if (a.n == 16) k = reinterpret_cast<const void*>(k_decode_groups<16>);
+  else if (a.n > 8) k = reinterpret_cast<const void*>(k_decode_groups_any<16>);
+  else if (a.n > 4) k = reinterpret_cast<const void*>(k_decode_groups_any<8>);
+  else if (a.n > 2) k = reinterpret_cast<const void*>(k_decode_groups_any<4>);
   return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
 }
 
