@@ -77,7 +77,9 @@ def test_batch_invariance_bitwise(model):
     for t in range(CAP):
         singles.append(run(m, x[t:t + 1], 0, N_LAYERS)[0])
         sids.append(ids[:, 0].cpu().numpy().copy())
-    for n in (4, 9, CAP):
+    # every decode kernel variant: one token; token groups of 2, 4, 8, 16 with
+    # and without idle groups (3, 7, 13); exact workgroup ranges (5, 9)
+    for n in (2, 3, 4, 5, 7, 9, 13, CAP):
         out = run(m, x[:n], 0, N_LAYERS)
         for t in range(n):
             assert np.array_equal(out[t], singles[t]), (n, t)
