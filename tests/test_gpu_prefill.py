@@ -45,6 +45,16 @@ def zipf():
 
 
 @pytest.fixture(scope="module")
+def scaled():
+    """One layer whose routed up-projection scales are multiplied by 4096 (the
+    stack's top layers): SwiGLU outputs pass fp16's range."""
+    synth = fg.Synth(FL, seed=7, n_layers=1, up_scale_mult={0: 4096})
+    m, ids, w = make_model(synth, 1)
+    yield synth, m, ids, w
+    m.close()
+
+
+@pytest.fixture(scope="module")
 def uniform():
     synth = fg.Synth(FL, seed=3, n_layers=1)
     m, ids, w = make_model(synth, 1)
@@ -130,3 +140,35 @@ def test_prefill_close_to_decode(uniform):
     for t in range(0, 17, 4):
         dec = run_forward(m, x[t:t + 1], 0, 1)[0]
         assert rel_l2(pre[t] - x[t], dec - x[t]) <= REL_L2_PREFILL
+
+
+@pytest.mark.parametrize("n", [33, 100, 1000])
+def test_prefill_mid_sizes_sampled(uniform, n):
+    """Token counts between the small cases and the full chunk: the first, the
+    last and a seeded sample of tokens against the oracle."""
+    synth, m, ids, w = uniform
+    x = fg.tokens(3, range(7000, 7000 + n))
+    out = run_forward(m, x, 0, 1)
+    assert np.all(np.isfinite(out))
+    rng = np.random.default_rng(n)
+    sample = sorted(set([0, n - 1] + rng.choice(n, 5, replace=False).tolist()))
+    errs = check_tokens(synth, 0, x, out, ids, w, sample, REL_L2_PREFILL)
+    print(f"n={n}: sampled rel-L2 max {max(errs):.2e}")
+
+
+def test_prefill_scaled_up_projection(scaled):
+    """x 4096 up-projection scales: h beyond fp16's range, kept as bf16 hi + lo."""
+    synth, m, ids, w = scaled
+    n = 64
+    x = fg.tokens(7, range(n))
+    out = run_forward(m, x, 0, 1)
+    assert np.all(np.isfinite(out))
+    src = SynthSource(synth)
+    hmax = 0.0
+    for t in (0, 21, 63):
+        err, res = check_layer(src, FL, 0, x[t], out[t], ids[0, t].cpu().numpy(), w[0, t].cpu().numpy(),
+                               tight=False)
+        assert err <= REL_L2_PREFILL, (t, err)
+        hmax = max(hmax, res.max_abs_h)
+    print(f"max |h| {hmax:.3g}")
+    assert hmax > 65504.0
