@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int w = blockIdx.x;
-  const int n = A.n;
+  constexpr int n = 1;   // this kernel runs one token; 2..16 run in the token-group kernels
   const bool poller = wave != PUB_WAVE;
 
   // Barrier that also tells every wave whether any thread timed out.  The
