@@ -112,6 +112,15 @@ struct Identity {
   __device__ int operator()(int j) const { return j; }
 };
 
+// (c, s) word j of a token, published as [c lo, c hi, s lo, s hi] per expert
+// (one aligned 32-byte store per expert) -> c[E] then s[E] as fp64 halves
+struct ZPos {
+  __device__ int operator()(int j) const {
+    const int e = j >> 2, p = j & 3;
+    return p < 2 ? 2 * e + p : 2 * E + 2 * e + (p - 2);
+  }
+};
+
 // h word j of a token (routed slots [TOPK][I], then shared [IS]) -> transposed position
 struct HPos {
   __device__ int operator()(int j) const {
@@ -170,7 +179,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   constexpr int HLOC = 2 * DECODE_MAX_TOKENS * TOPK * DECODE_MAX_TOKENS + 4 * DECODE_MAX_TOKENS;
   __shared__ float hloc[HLOC];
   __shared__ int hloc_idx[HLOC];
-  __shared__ int n_hloc;
   __shared__ float xnew[DECODE_MAX_TOKENS][8];
   __shared__ int ids_l[DECODE_MAX_TOKENS][TOPK];
   __shared__ float w_l[DECODE_MAX_TOKENS][TOPK];
@@ -263,22 +271,13 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     }
     wg_sync();
     PUB_MARK(11);
-    if (wave == PUB_WAVE && lane < n) {
-      const int t = lane;
+    if (wave == PUB_WAVE && lane < 4) {   // lane p writes word p of [c lo, c hi, s lo, s hi]: one 32-byte store
       double sv, cv;
-      router_scores(zpart[t], p1_bias, sv, cv);
-      const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
-      const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
-      uint64_t* z = A.xz + (size_t)t * 4 * E;
-      publish(z + 2 * w, tag, (uint32_t)cb);
-      publish(z + 2 * w + 1, tag, (uint32_t)(cb >> 32));
-      publish(z + 2 * E + 2 * w, tag, (uint32_t)sb);
-      publish(z + 2 * E + 2 * w + 1, tag, (uint32_t)(sb >> 32));
+      router_scores(zpart[0], p1_bias, sv, cv);
+      const unsigned long long v = (unsigned long long)__double_as_longlong(lane < 2 ? cv : sv);
+      publish(A.xz + 4 * w + lane, tag, (lane & 1) ? (uint32_t)(v >> 32) : (uint32_t)v);
     }
-    if (wave == PUB_WAVE && l + 1 < A.l1) {
-      p1_copy(l + 1);
-      wait_all_memory();   // the other waves gather (c, s) meanwhile
-    }
+
     PUB_MARK(12);
     PHASE_MARK(3);
     PHASE_MARK(4);
@@ -289,8 +288,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       for (int i = 0; i < nb; ++i) {
         bool ok = true;
         if (poller)
-          ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag,
-                                                                    zbuf[i], A.err, Identity(), tid, l,
+          ok = gather<(4 * E + NPOLL - 1) / NPOLL, ZPos, NPOLL>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag,
+                                                                zbuf[i], A.err, ZPos(), tid, l,
                                                                     (t0 + i == 0) ? 1 : -1, gts_lds);
         if (sync_or(!ok)) return;
       }
@@ -312,7 +311,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     // distinct experts of the call (for one token: its six picks, in pick order)
     const int D = (n == 1) ? TOPK : distinct_experts(ids_l, n, list, wave_tot);
     const int* dl = (n == 1) ? ids_l[0] : list;
-    if (tid == 0) n_hloc = 0;
     PHASE_MARK(7);
     // down codes of the first token for output row 8 w + wave: needed after the
     // h exchange; loaded now so that nothing slow is in flight while polling
@@ -344,11 +342,12 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
           }
         }
       };
-      auto emit = [&](int word, float hv) {   // one h value of this workgroup, by lane 0
+      // one h value per task j, kept in task order so that the publisher's
+      // lanes write consecutive words (whole 32-byte pieces)
+      auto emit = [&](int j, int word, float hv) {
         if (lane == 0) {
-          const int k = atomicAdd(&n_hloc, 1);   // < HLOC: see the bound above
-          hloc[k] = hv;
-          hloc_idx[k] = word;
+          hloc[j] = hv;
+          hloc_idx[j] = word;
         }
       };
       auto compute_batch = [&](int j0) {
@@ -361,17 +360,16 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
           for (int t = 0; t < n; ++t) {
             const int slot = slot_of(ids_l[t], e);
             if (slot < 0) continue;
-            emit(t * HW + slot * I + r, gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds[t], asum_lds[t][lane]));
+            emit(j, t * HW + slot * I + r, gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds[t], asum_lds[t][lane]));
           }
         }
       };
-      wg_sync();   // n_hloc reset visible
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
       if (wave < 4) {   // the shared row (weights already here) while the routed loads fly
         const int r = w * 4 + wave;
         for (int t = 0; t < n; ++t)
-          emit(t * HW + TOPK * I + r,
+          emit(wave, t * HW + TOPK * I + r,
                gateup_row_token(p1_code[l & 1][0][wave][lane], p1_scale[l & 1][0][wave * (H / G) + (lane >> 2)],
                                 p1_code[l & 1][1][wave][lane], p1_scale[l & 1][1][wave * (H / G) + (lane >> 2)],
                                 a_lds[t], asum_lds[t][lane]));
@@ -385,11 +383,15 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     wg_sync();
     PUB_MARK(13);
     if (wave == PUB_WAVE) {
-      const int cnt = n_hloc;
+      const int cnt = 4 + 2 * D;   // one value per task (one token)
       for (int k = lane; k < cnt; k += 64) {
         const int word = hloc_idx[k];
         if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (l + 1 < A.l1) {
+        p1_copy(l + 1);
+        wait_all_memory();   // the other waves gather h meanwhile
       }
     }
     PUB_MARK(14);
@@ -464,7 +466,6 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
   float* const hbuf = reinterpret_cast<float*>(stage);
   __shared__ float hloc[NTASK];
   __shared__ int hloc_idx[NTASK];
-  __shared__ int n_hloc;
   __shared__ float xnew[NOUT];
   __shared__ int ids_l[TOPK];
   __shared__ float w_l[TOPK];
@@ -522,30 +523,31 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       if (lane == 0) zpart[j][wave] = p;
     }
     wg_sync();
-    if (wave == PUB_WAVE && lane < K) {
-      const int e = K * u + lane;
-      double sv, cv;
-      router_scores(zpart[lane], L.bias[e], sv, cv);
-      const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
-      const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
-      uint64_t* z = A.xz + (size_t)t * 4 * E;
-      publish(z + 2 * e, tag, (uint32_t)cb);
-      publish(z + 2 * e + 1, tag, (uint32_t)(cb >> 32));
-      publish(z + 2 * E + 2 * e, tag, (uint32_t)sb);
-      publish(z + 2 * E + 2 * e + 1, tag, (uint32_t)(sb >> 32));
+    if (wave == PUB_WAVE) {   // lane L writes word L % 4 of expert K u + L / 4: one store of 4 K words
+      unsigned long long cb = 0, sb = 0;
+      if (lane < K) {
+        double sv, cv;
+        router_scores(zpart[lane], L.bias[K * u + lane], sv, cv);
+        cb = (unsigned long long)__double_as_longlong(cv);
+        sb = (unsigned long long)__double_as_longlong(sv);
+      }
+      const int src = lane >> 2, pw = lane & 3;
+      const uint32_t c_lo = __shfl((uint32_t)cb, src), c_hi = __shfl((uint32_t)(cb >> 32), src);
+      const uint32_t s_lo = __shfl((uint32_t)sb, src), s_hi = __shfl((uint32_t)(sb >> 32), src);
+      if (lane < 4 * K)
+        publish(A.xz + (size_t)t * 4 * E + 4 * K * u + lane, tag, pw == 0 ? c_lo : pw == 1 ? c_hi : pw == 2 ? s_lo : s_hi);
     }
 
     // ---------------- P2: routing, gate/up
     ok = true;
     if (poller)
-      ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
-                                                                Identity(), tid, l, -1, gts_lds);
+      ok = gather<(4 * E + NPOLL - 1) / NPOLL, ZPos, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
+                                                            ZPos(), tid, l, -1, gts_lds);
     if (sync_or(!ok)) return;
     if (wave == 0) {
       const double* zc = reinterpret_cast<const double*>(stage);
       route_token(zc, zc + E, ids_l, w_l);
     }
-    if (tid == 0) n_hloc = 0;
     wg_sync();
     if (u == 0 && A.trace_ids && wave == PUB_WAVE && lane < TOPK) {
       const size_t o = ((size_t)l * A.trace_cap + t) * TOPK + lane;
@@ -598,10 +600,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
           if (j >= NTASK) break;
           const int word = j < NSH ? TOPK * I + NSH * u + j : NRT * u + (j - NSH);   // slot * I + row
           const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
-          if (lane == 0) {
-            const int k = atomicAdd(&n_hloc, 1);   // < NTASK: one value per task
-            hloc[k] = hv;
-            hloc_idx[k] = word;
+          if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
+            hloc[j] = hv;
+            hloc_idx[j] = word;
           }
         }
       };
@@ -612,8 +613,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
     }
     wg_sync();
     if (wave == PUB_WAVE) {
-      const int cnt = n_hloc;
-      for (int k = lane; k < cnt; k += 64) {
+      for (int k = lane; k < NTASK; k += 64) {   // one value per task
         const int word = hloc_idx[k];
         if (word >= 0 && word < HW) publish(A.xh + (size_t)t * HW + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -683,7 +683,6 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
   float* const hbuf = reinterpret_cast<float*>(stage);
   __shared__ float hloc[MTASK];
   __shared__ int hloc_idx[MTASK];
-  __shared__ int n_hloc;
   __shared__ float xnew[MOUT];
   __shared__ int ids_l[TOPK];
   __shared__ float w_l[TOPK];
@@ -750,30 +749,31 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
       }
     }
     wg_sync();
-    if (wave == PUB_WAVE && lane < nr) {
-      const int e = r0 + lane;
-      double sv, cv;
-      router_scores(zpart[lane], L.bias[e], sv, cv);
-      const unsigned long long cb = (unsigned long long)__double_as_longlong(cv);
-      const unsigned long long sb = (unsigned long long)__double_as_longlong(sv);
-      uint64_t* z = A.xz + (size_t)t * 4 * E;
-      publish(z + 2 * e, tag, (uint32_t)cb);
-      publish(z + 2 * e + 1, tag, (uint32_t)(cb >> 32));
-      publish(z + 2 * E + 2 * e, tag, (uint32_t)sb);
-      publish(z + 2 * E + 2 * e + 1, tag, (uint32_t)(sb >> 32));
+    if (wave == PUB_WAVE) {   // lane L writes word L % 4 of expert r0 + L / 4: one store of 4 nr words
+      unsigned long long cb = 0, sb = 0;
+      if (lane < nr) {
+        double sv, cv;
+        router_scores(zpart[lane], L.bias[r0 + lane], sv, cv);
+        cb = (unsigned long long)__double_as_longlong(cv);
+        sb = (unsigned long long)__double_as_longlong(sv);
+      }
+      const int src = lane >> 2, pw = lane & 3;
+      const uint32_t c_lo = __shfl((uint32_t)cb, src), c_hi = __shfl((uint32_t)(cb >> 32), src);
+      const uint32_t s_lo = __shfl((uint32_t)sb, src), s_hi = __shfl((uint32_t)(sb >> 32), src);
+      if (lane < 4 * nr)
+        publish(A.xz + (size_t)t * 4 * E + 4 * r0 + lane, tag, pw == 0 ? c_lo : pw == 1 ? c_hi : pw == 2 ? s_lo : s_hi);
     }
 
     // ---------------- P2: routing, gate/up
     ok = true;
     if (poller)
-      ok = gather<(4 * E + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
-                                                                Identity(), tid, l, -1, gts_lds);
+      ok = gather<(4 * E + NPOLL - 1) / NPOLL, ZPos, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
+                                                            ZPos(), tid, l, -1, gts_lds);
     if (sync_or(!ok)) return;
     if (wave == 0) {
       const double* zc = reinterpret_cast<const double*>(stage);
       route_token(zc, zc + E, ids_l, w_l);
     }
-    if (tid == 0) n_hloc = 0;
     wg_sync();
     if (u == 0 && A.trace_ids && wave == PUB_WAVE && lane < TOPK) {
       const size_t o = ((size_t)l * A.trace_cap + t) * TOPK + lane;
@@ -813,10 +813,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
           if (j >= ntask) break;
           const int word = j < nsh ? TOPK * I + s0 + j : q0 + (j - nsh);   // slot * I + row
           const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
-          if (lane == 0) {
-            const int k = atomicAdd(&n_hloc, 1);   // < ntask <= MTASK: one value per task
-            hloc[k] = hv;
-            hloc_idx[k] = word;
+          if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
+            hloc[j] = hv;
+            hloc_idx[j] = word;
           }
         }
       };
@@ -827,8 +826,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
     }
     wg_sync();
     if (wave == PUB_WAVE) {
-      const int cnt = n_hloc;
-      for (int k = lane; k < cnt; k += 64) {
+      for (int k = lane; k < ntask; k += 64) {   // one value per task
         const int word = hloc_idx[k];
         if (word >= 0 && word < HW) publish(A.xh + (size_t)t * HW + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
