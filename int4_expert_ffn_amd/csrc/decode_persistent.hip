@@ -167,9 +167,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   // wave: router row w (uint2 t for thread t) and bias[w] of the current
   // layer; shared-expert gate (g = 0) and up (g = 1) rows 4 w + v, v < 4
   // (uint4 per lane) with their 16 scales each, for layer l in buffer l & 1.
-  // The next layer's copy is issued right after this layer's (c, s) are
-  // published: the router row and bias have been used by then, and the other
-  // shared-row buffer is free.  It completes while the (c, s) are gathered.
+  // Each later layer's copy is issued at the start of that layer, while the
+  // other waves gather x (the previous layer has used the router row and the
+  // bias by then), and is complete before the barrier that ends the gather.
   __shared__ __align__(16) uint2 p1_router[NT];
   __shared__ __align__(16) uint4 p1_code[2][2][4][64];
   __shared__ __align__(16) uint16_t p1_scale[2][2][4 * (H / G)];
@@ -241,6 +241,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
 
+    // this layer's P1 weights (the first layer's were copied before the
+    // loop), while the other waves gather x
+    if (wave == PUB_WAVE && l > A.l0) p1_copy(l);
+
     // ---------------- P0: block input of every token
     PHASE_MARK(0);
     for (int t = 0; t < n; ++t) {
@@ -252,6 +256,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
                                                             reinterpret_cast<uint32_t*>(xstage), A.err, Identity(),
                                                             tid, l, t == 0 ? 0 : -1, gts_lds);
       }
+      if (wave == PUB_WAVE) wait_all_memory();   // the P1 copy is in LDS before the next barrier
       if (sync_or(!ok)) return;
       if (t == 0) PHASE_MARK(1);
       const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
@@ -388,10 +393,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         const int word = hloc_idx[k];
         if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (l + 1 < A.l1) {
-        p1_copy(l + 1);
-        wait_all_memory();   // the other waves gather h meanwhile
       }
     }
     PUB_MARK(14);
