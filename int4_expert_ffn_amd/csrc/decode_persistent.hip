@@ -129,6 +129,17 @@ struct HPos {
   }
 };
 
+// Single-token h exchange, workgroup-major: workgroup w's 16 values (4 shared
+// rows 4 w .., then 12 routed rows 12 w .. of the six slots) are the 128-byte
+// run of words 16 w .. 16 w + 15, written by one store.  Word j -> h index ->
+// transposed position.
+struct HPosWG {
+  __device__ int operator()(int j) const {
+    const int w = j >> 4, k = j & 15;
+    return HPos()(k < 4 ? TOPK * I + 4 * w + k : 12 * w + (k - 4));
+  }
+};
+
 // Asynchronous copy of 16 (or 4) bytes per lane from global memory into LDS:
 // lane i's bytes land at lds + i * size.  Completion is counted by the
 // wave's memory counter like a load; nothing is written to registers.
@@ -391,7 +402,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       const int cnt = 4 + 2 * D;   // one value per task (one token)
       for (int k = lane; k < cnt; k += 64) {
         const int word = hloc_idx[k];
-        if (word >= 0 && word < n * HW) publish(A.xh + word, tag + 1, __float_as_uint(hloc[k]));
+        // one 128-byte run per workgroup (the h words of its tasks, in task order)
+        if (word >= 0 && word < n * HW) publish(A.xh + 16 * w + k, tag + 1, __float_as_uint(hloc[k]));
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -405,8 +417,8 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       if (t > 0) load_down_row(L, ids_l[t], row, ca, sa, cb, sb);
       bool ok = true;
       if (poller)
-        ok = gather<(HW + NPOLL - 1) / NPOLL, HPos, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
-                                                          reinterpret_cast<uint32_t*>(hbuf), A.err, HPos(), tid, l,
+        ok = gather<(HW + NPOLL - 1) / NPOLL, HPosWG, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
+                                                            reinterpret_cast<uint32_t*>(hbuf), A.err, HPosWG(), tid, l,
                                                           t == 0 ? 2 : -1, gts_lds);
       if (sync_or(!ok)) return;
       if (t == 0) PHASE_MARK(9);
