@@ -140,21 +140,6 @@ struct HPosWG {
   }
 };
 
-// Asynchronous copy of 16 (or 4) bytes per lane from global memory into LDS:
-// lane i's bytes land at lds + i * size.  Completion is counted by the
-// wave's memory counter like a load; nothing is written to registers.
-typedef __attribute__((address_space(1))) void gmem_void;
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void copy_to_lds16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((gmem_void*)src, (lds_void*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void copy_to_lds4(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds((gmem_void*)src, (lds_void*)lds, 4, 0, 0);
-}
-
-// Wait until every memory operation this wave has issued is complete.
-__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
 // Role split inside a workgroup: on GFX9 a wavefront's memory counter retires
 // loads and stores in issue order, so a poll issued after a store waits for
 // that store's acknowledgement.  The last wave publishes each exchange (from
@@ -174,17 +159,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   uint32_t (*const zbuf)[4 * E] = reinterpret_cast<uint32_t (*)[4 * E]>(stage);
   float* const hbuf = reinterpret_cast<float*>(stage);
   static_assert(H <= HW && 4 * 4 * E <= HW, "gather staging too small");
-  // This workgroup's P1 weights, copied from global memory by the publisher
-  // wave: router row w (uint2 t for thread t) and bias[w] of the current
-  // layer; shared-expert gate (g = 0) and up (g = 1) rows 4 w + v, v < 4
-  // (uint4 per lane) with their 16 scales each, for layer l in buffer l & 1.
-  // Each later layer's copy is issued at the start of that layer, while the
-  // other waves gather x (the previous layer has used the router row and the
-  // bias by then), and is complete before the barrier that ends the gather.
-  __shared__ __align__(16) uint2 p1_router[NT];
-  __shared__ __align__(16) uint4 p1_code[2][2][4][64];
-  __shared__ __align__(16) uint16_t p1_scale[2][2][4 * (H / G)];
-  __shared__ __align__(16) float p1_bias;
   // this workgroup's h values before publication: at most 2 D routed rows
   // (D <= 16 * 6 distinct experts) times 16 tokens, plus 4 shared rows x 16
   constexpr int HLOC = 2 * DECODE_MAX_TOKENS * TOPK * DECODE_MAX_TOKENS + 4 * DECODE_MAX_TOKENS;
@@ -226,35 +200,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   };
   wg_sync();
 
-  // publisher wave: copy layer l's P1 weights into LDS (14 instructions)
-  auto p1_copy = [&](int l) {
-    const LayerW L = layer_at(A.base, A.layer_stride, l);
-    const int b = l & 1;
-    const uint4* rr = reinterpret_cast<const uint4*>(L.router + (size_t)w * H);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) copy_to_lds16(rr + 64 * k + lane, reinterpret_cast<uint4*>(p1_router) + 64 * k);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      copy_to_lds16(reinterpret_cast<const uint4*>(L.sh_gate + (size_t)(4 * w + v) * (H / 2)) + lane, p1_code[b][0][v]);
-      copy_to_lds16(reinterpret_cast<const uint4*>(L.sh_up + (size_t)(4 * w + v) * (H / 2)) + lane, p1_code[b][1][v]);
-    }
-    // scales of rows 4 w .. 4 w + 3: gate on lanes 0..31, up on 32..63 (two per lane)
-    const uint16_t* sc = (lane < 32 ? L.sh_gate_s : L.sh_up_s) + (size_t)4 * w * (H / G) + 2 * (lane & 31);
-    copy_to_lds4(sc, p1_scale[b]);
-    if (lane == 0) copy_to_lds4(L.bias + w, &p1_bias);
-  };
-  if (wave == PUB_WAVE) {
-    p1_copy(A.l0);
-    wait_all_memory();
-  }
-
   for (int l = A.l0; l < A.l1; ++l) {
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
 
-    // this layer's P1 weights (the first layer's were copied before the
-    // loop), while the other waves gather x
-    if (wave == PUB_WAVE && l > A.l0) p1_copy(l);
+    // this workgroup's router row (8 bytes per thread) and bias, requested
+    // before the x exchange so that its wait hides them
+    const uint2 rw = load_router_part(L.router + (size_t)w * H);
+    const float bias_w = L.bias[w];
 
     // ---------------- P0: block input of every token
     PHASE_MARK(0);
@@ -267,7 +220,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
                                                             reinterpret_cast<uint32_t*>(xstage), A.err, Identity(),
                                                             tid, l, t == 0 ? 0 : -1, gts_lds);
       }
-      if (wave == PUB_WAVE) wait_all_memory();   // the P1 copy is in LDS before the next barrier
       if (sync_or(!ok)) return;
       if (t == 0) PHASE_MARK(1);
       const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
@@ -282,18 +234,29 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     // ---------------- P1: router row w over all waves -> the publisher wave writes (c, s)
     PHASE_MARK(2);
     for (int t = 0; t < n; ++t) {
-      const double p = router_part(p1_router[tid], a_lds[t]);
+      const double p = router_part(rw, a_lds[t]);
       if (lane == 0) zpart[t][wave] = p;
     }
     wg_sync();
     PUB_MARK(11);
     if (wave == PUB_WAVE && lane < 4) {   // lane p writes word p of [c lo, c hi, s lo, s hi]: one 32-byte store
       double sv, cv;
-      router_scores(zpart[0], p1_bias, sv, cv);
+      router_scores(zpart[0], bias_w, sv, cv);
       const unsigned long long v = (unsigned long long)__double_as_longlong(lane < 2 ? cv : sv);
       publish(A.xz + 4 * w + lane, tag, (lane & 1) ? (uint32_t)(v >> 32) : (uint32_t)v);
     }
 
+    // shared-expert gate/up row 4 w + wave of waves 0..3, requested before the
+    // (c, s) exchange so that its wait hides them
+    uint4 shg = make_uint4(0u, 0u, 0u, 0u), shu = shg;
+    uint32_t shsg = 0u, shsu = 0u;
+    if (wave < 4) {
+      const size_t r = (size_t)4 * w + wave;
+      shg = reinterpret_cast<const uint4*>(L.sh_gate + r * (H / 2))[lane];
+      shu = reinterpret_cast<const uint4*>(L.sh_up + r * (H / 2))[lane];
+      shsg = L.sh_gate_s[r * (H / G) + (lane >> 2)];
+      shsu = L.sh_up_s[r * (H / G) + (lane >> 2)];
+    }
     PUB_MARK(12);
     PHASE_MARK(3);
     PHASE_MARK(4);
@@ -382,13 +345,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       };
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
-      if (wave < 4) {   // the shared row (weights already here) while the routed loads fly
+      if (wave < 4) {   // the shared row (its weights requested earlier) while the routed loads fly
         const int r = w * 4 + wave;
         for (int t = 0; t < n; ++t)
           emit(wave, t * HW + TOPK * I + r,
-               gateup_row_token(p1_code[l & 1][0][wave][lane], p1_scale[l & 1][0][wave * (H / G) + (lane >> 2)],
-                                p1_code[l & 1][1][wave][lane], p1_scale[l & 1][1][wave * (H / G) + (lane >> 2)],
-                                a_lds[t], asum_lds[t][lane]));
+               gateup_row_token(shg, shsg, shu, shsu, a_lds[t], asum_lds[t][lane]));
       }
       compute_batch(j0);
       for (j0 += TB * NWAVES; j0 < 4 + R; j0 += TB * NWAVES) {
