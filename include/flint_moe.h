@@ -96,7 +96,9 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
  * is allowed; partial overlap is not.  1 <= n_tokens <= FLINT_MAX_TOKENS and
  * 0 <= layer_begin < layer_end <= n_layers.  Asynchronous on `stream` (a
  * hipStream_t; NULL = the default stream).  One handle serves one stream at a
- * time: calls on a handle must not overlap.  For n_tokens <= 16 each token's
+ * time: calls on a handle must not overlap.  A call must not be captured into
+ * a HIP graph for replay: each call takes per-call state from the host (the
+ * tags and slot parity of its exchanges between workgroups).  For n_tokens <= 16 each token's
  * result is bitwise independent of n_tokens (decode path).  Larger calls take
  * the prefill path: tokens sorted by expert, grouped GEMMs on the matrix
  * cores, the SwiGLU output kept as two bf16 parts (about 16 significant bits)

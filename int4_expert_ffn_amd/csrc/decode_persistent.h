@@ -20,7 +20,18 @@ struct PersistArgs {
   int trace_cap;
   int* err;                // device error word
   uint32_t epoch;          // tag base of this call (multiple of 256, never 0)
+  // Single-token exchanges of x and h: untagged 32-bit values in one slot per
+  // layer and call parity, re-armed to EMPTY_WORD by the call of the other parity.
+  uint32_t* vx;            // [2][n_layers][H] residual after each layer
+  uint32_t* vh;            // [2][n_layers][TOPK*I + IS] h of each layer, workgroup-major
+  int n_layers;            // layers of the handle (every one is re-armed)
+  int parity;              // half of vx / vh that this call writes
 };
+
+// Value of an exchange slot that has not been written in the current call (a
+// NaN pattern that published values never carry: NaNs are published as the
+// canonical quiet NaN).
+constexpr uint32_t EMPTY_WORD = 0xFFFFFFFFu;
 
 __host__ __device__ inline LayerW layer_at(const LayerW& b, size_t stride, int l) {
   const size_t o = stride * (size_t)l;
@@ -47,6 +58,10 @@ __host__ __device__ inline LayerW layer_at(const LayerW& b, size_t stride, int l
 constexpr size_t XZ_WORDS = (size_t)DECODE_MAX_TOKENS * E * 4;
 constexpr size_t XH_WORDS = (size_t)DECODE_MAX_TOKENS * (TOPK * I + IS);
 constexpr size_t XX_WORDS = (size_t)DECODE_MAX_TOKENS * H;
+
+// 32-bit words in each single-token exchange slot array (both parities)
+inline size_t vx_words(int n_layers) { return (size_t)2 * n_layers * H; }
+inline size_t vh_words(int n_layers) { return (size_t)2 * n_layers * (TOPK * I + IS); }
 
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s);
 hipError_t clear_exchange(uint64_t* p, size_t n_words, hipStream_t s);

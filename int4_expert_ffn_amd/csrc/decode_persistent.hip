@@ -108,6 +108,81 @@ __device__ __forceinline__ bool gather(const uint64_t* src, int nwords, uint32_t
   return true;
 }
 
+// Single-token exchanges without tags.  A slot holds EMPTY_WORD until its
+// producer stores the value with one 32-bit store, so a reader that sees
+// anything else sees the whole value.  Pollers read 16 bytes per load with the
+// sc1 cache policy, the policy the compiler gives agent-scope atomic loads on
+// this chip: the load is served from the device-coherent level, never from a
+// workgroup's or an XCD's stale copy.  Half the bytes of the tagged words, a
+// quarter of the load instructions.
+__device__ __forceinline__ void publish_value(uint32_t* p, float v) {
+  const uint32_t u = (v != v) ? 0x7FC00000u : __float_as_uint(v);   // never EMPTY_WORD
+  __hip_atomic_store(p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint4 load_values16(__amdgpu_buffer_rsrc_t rs, int byte_offset) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  constexpr int SC1 = 16;   // cache-policy bit of the buffer instructions
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_offset, 0, SC1);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ bool has_empty(uint4 v) {
+  return v.x == EMPTY_WORD || v.y == EMPTY_WORD || v.z == EMPTY_WORD || v.w == EMPTY_WORD;
+}
+
+// Wait until values src[0..nvals) (nvals a multiple of 4) are all written;
+// store value j in dst[pos(j)].  Thread i polls the 16-byte groups i + NTHR k,
+// k < K.  Returns false on timeout (the device error word is then set).
+template <int K, typename Pos, int NTHR = NT>
+__device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, uint32_t* dst, int* err, Pos pos,
+                                              int tid, int dbg_layer, int dbg_id, GtsLds gts_lds) {
+  GATHER_PROBE(0, wall_clock64());
+  unsigned long long iters = 0;
+  const int ngroups = nvals >> 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(src), 0, nvals * 4,
+                                                                      0x00020000);
+  uint4 v[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = tid + NTHR * k;
+    v[k] = (j < ngroups) ? load_values16(rs, 16 * j) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const long long t0 = wall_clock64();
+  while (true) {
+    // the buffer loads are plain reads to the compiler: keep each round's
+    // loads from being merged with the previous round's
+    asm volatile("" ::: "memory");
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (has_empty(v[k])) {
+        all = false;
+        v[k] = load_values16(rs, 16 * (tid + NTHR * k));
+      }
+    }
+    if (iters++ == 0) GATHER_PROBE(1, wall_clock64());
+    if (all) break;
+    if (wall_clock64() - t0 > SPIN_TICKS) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+  }
+  GATHER_PROBE(2, wall_clock64());
+  GATHER_PROBE(3, iters);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = tid + NTHR * k;
+    if (j < ngroups) {
+      dst[pos(4 * j)] = v[k].x;
+      dst[pos(4 * j + 1)] = v[k].y;
+      dst[pos(4 * j + 2)] = v[k].z;
+      dst[pos(4 * j + 3)] = v[k].w;
+    }
+  }
+  return true;
+}
+
 struct Identity {
   __device__ int operator()(int j) const { return j; }
 };
@@ -198,11 +273,26 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     bail_par ^= 1;
     return r;
   };
+  // Re-arm this workgroup's slots of the other parity for every layer (its x
+  // rows 8 w .. 8 w + 7 and h words 16 w .. 16 w + 15): the next call writes
+  // them.  Runs on every way out of the kernel.
+  const int other = A.parity ^ 1;
+  auto rearm = [&]() {
+    if (wave != PUB_WAVE) return;
+    const uint4 empty = make_uint4(EMPTY_WORD, EMPTY_WORD, EMPTY_WORD, EMPTY_WORD);
+    for (int i = lane; i < 6 * A.n_layers; i += 64) {
+      const int lc = i / 6, q = i % 6;
+      const size_t slot = (size_t)other * A.n_layers + lc;
+      uint32_t* p = q < 2 ? A.vx + slot * H + 8 * w + 4 * q : A.vh + slot * HW + 16 * w + 4 * (q - 2);
+      *reinterpret_cast<uint4*>(p) = empty;
+    }
+  };
   wg_sync();
 
   for (int l = A.l0; l < A.l1; ++l) {
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
+    uint32_t* const vh_l = A.vh + ((size_t)A.parity * A.n_layers + l) * HW;
 
     // this workgroup's router row (8 bytes per thread) and bias, requested
     // before the x exchange so that its wait hides them
@@ -216,11 +306,11 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       if (l == A.l0) {
         if (tid < H / 4) reinterpret_cast<float4*>(xstage)[tid] = reinterpret_cast<const float4*>(A.x + (size_t)t * H)[tid];
       } else if (poller) {
-        ok = gather<(H + NPOLL - 1) / NPOLL, Identity, NPOLL>(A.xx + (size_t)t * H, H, tag - 4 + 2,
-                                                            reinterpret_cast<uint32_t*>(xstage), A.err, Identity(),
-                                                            tid, l, t == 0 ? 0 : -1, gts_lds);
+        ok = gather_values<(H / 4 + NPOLL - 1) / NPOLL, Identity, NPOLL>(
+            A.vx + ((size_t)A.parity * A.n_layers + (l - 1)) * H, H, reinterpret_cast<uint32_t*>(xstage), A.err,
+            Identity(), tid, l, 0, gts_lds);
       }
-      if (sync_or(!ok)) return;
+      if (sync_or(!ok)) { rearm(); return; }
       if (t == 0) PHASE_MARK(1);
       const float4 xv = reinterpret_cast<const float4*>(xstage)[tid];
       if ((tid >> 1) == w) {   // this workgroup's 8 output rows, kept for the residual
@@ -270,7 +360,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
           ok = gather<(4 * E + NPOLL - 1) / NPOLL, ZPos, NPOLL>(A.xz + (size_t)(t0 + i) * 4 * E, 4 * E, tag,
                                                                 zbuf[i], A.err, ZPos(), tid, l,
                                                                     (t0 + i == 0) ? 1 : -1, gts_lds);
-        if (sync_or(!ok)) return;
+        if (sync_or(!ok)) { rearm(); return; }
       }
       PHASE_MARK(5);
       if (wave < nb) {
@@ -364,7 +454,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       for (int k = lane; k < cnt; k += 64) {
         const int word = hloc_idx[k];
         // one 128-byte run per workgroup (the h words of its tasks, in task order)
-        if (word >= 0 && word < n * HW) publish(A.xh + 16 * w + k, tag + 1, __float_as_uint(hloc[k]));
+        if (word >= 0 && word < n * HW) publish_value(vh_l + 16 * w + k, hloc[k]);
         else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -378,10 +468,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       if (t > 0) load_down_row(L, ids_l[t], row, ca, sa, cb, sb);
       bool ok = true;
       if (poller)
-        ok = gather<(HW + NPOLL - 1) / NPOLL, HPosWG, NPOLL>(A.xh + (size_t)t * HW, HW, tag + 1,
-                                                            reinterpret_cast<uint32_t*>(hbuf), A.err, HPosWG(), tid, l,
-                                                          t == 0 ? 2 : -1, gts_lds);
-      if (sync_or(!ok)) return;
+        ok = gather_values<(HW / 4 + NPOLL - 1) / NPOLL, HPosWG, NPOLL>(
+            vh_l, HW, reinterpret_cast<uint32_t*>(hbuf), A.err, HPosWG(), tid, l, 2, gts_lds);
+      if (sync_or(!ok)) { rearm(); return; }
       if (t == 0) PHASE_MARK(9);
       const int sub = lane & 15;
       auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
@@ -397,13 +486,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       for (int i = lane; i < 8 * n; i += 64) {
         const int t = i >> 3, r = NWAVES * w + (i & 7);
         const float v = xnew[t][i & 7];
-        if (l + 1 < A.l1) publish(A.xx + (size_t)t * H + r, tag + 2, __float_as_uint(v));
+        if (l + 1 < A.l1) publish_value(A.vx + ((size_t)A.parity * A.n_layers + l) * H + r, v);
         else A.out[(size_t)t * H + r] = v;
       }
     }
     PUB_MARK(15);
     PHASE_MARK(10);
   }
+  rearm();
 #ifdef FLINT_PHASE_TS
   if (threadIdx.x == 0) {
     for (int l = A.l0; l < A.l1 && l < TS_LAYERS; ++l) {

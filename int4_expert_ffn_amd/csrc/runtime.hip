@@ -74,6 +74,9 @@ struct flint_moe {
   uint64_t* xh = nullptr;
   uint64_t* xx = nullptr;
   uint32_t epoch = 0;
+  uint32_t* vx = nullptr;   // single-token exchange slots, two call parities
+  uint32_t* vh = nullptr;
+  int parity = 0;           // parity of the next single-token call
 };
 
 static void release(flint_moe* h) {
@@ -87,6 +90,8 @@ static void release(flint_moe* h) {
   if (h->xz) (void)hipFree(h->xz);
   if (h->xh) (void)hipFree(h->xh);
   if (h->xx) (void)hipFree(h->xx);
+  if (h->vx) (void)hipFree(h->vx);
+  if (h->vh) (void)hipFree(h->vh);
   delete h;
 }
 
@@ -197,11 +202,16 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
     if (!rc) rc = checked_malloc((void**)&h->xz, XZ_WORDS * 8, "exchange z");
     if (!rc) rc = checked_malloc((void**)&h->xh, XH_WORDS * 8, "exchange h");
     if (!rc) rc = checked_malloc((void**)&h->xx, XX_WORDS * 8, "exchange x");
+    if (!rc) rc = checked_malloc((void**)&h->vx, vx_words(n_layers) * 4, "exchange slots x");
+    if (!rc) rc = checked_malloc((void**)&h->vh, vh_words(n_layers) * 4, "exchange slots h");
     if (rc) { release(h); return rc; }
     e = hipMemcpy(h->layers_dev, h->layers.data(), sizeof(LayerW) * n_layers, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(h->xz, 0, XZ_WORDS * 8);
     if (e == hipSuccess) e = hipMemset(h->xh, 0, XH_WORDS * 8);
     if (e == hipSuccess) e = hipMemset(h->xx, 0, XX_WORDS * 8);
+    static_assert(EMPTY_WORD == 0xFFFFFFFFu, "slots are armed with 0xFF bytes");
+    if (e == hipSuccess) e = hipMemset(h->vx, 0xFF, vx_words(n_layers) * 4);
+    if (e == hipSuccess) e = hipMemset(h->vh, 0xFF, vh_words(n_layers) * 4);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) { rc = fail_hip(e, "create"); release(h); return rc; }
@@ -253,8 +263,15 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
     a.trace_cap = h->trace_capacity;
     a.err = h->dev_error;
     a.epoch = h->epoch;
+    a.vx = h->vx;
+    a.vh = h->vh;
+    a.n_layers = h->n_layers;
+    a.parity = h->parity;
     e = launch_decode_persistent(a, s);
     if (e != hipSuccess) return fail_hip(e, "persistent decode launch");
+    // a single-token call writes the slots of its parity and re-arms the
+    // others, which the next single-token call then uses
+    if (n_tokens == 1) h->parity ^= 1;
     return FLINT_OK;
   }
   for (int l = layer_begin; l < layer_end; ++l) {

@@ -182,3 +182,38 @@ def test_persistent_and_layered_modes_agree_bitwise(model):
         m2.status()
     finally:
         m2.close()
+
+
+def test_single_token_exchange_slots_across_mixed_calls(model):
+    """Single-token calls pass x and h between workgroups through per-layer
+    slots of two call parities, each call re-arming the other parity's slots.
+    A queued mix of single-token calls over varied layer ranges, with token
+    group calls between them, must match the per-layer kernels bitwise; a slot
+    left holding an earlier call's value would be read as fresh and show here."""
+    synth, m, ids, w = model
+    layers = build_layers(synth, range(N_LAYERS))
+    os.environ["FLINT_MOE_DECODE"] = "layered"
+    try:
+        ref = F.FlintMoE(layers)
+    finally:
+        del os.environ["FLINT_MOE_DECODE"]
+    del layers
+    rng = np.random.default_rng(11)
+    x = torch.from_numpy(fg.tokens(0, range(700, 716))).cuda()
+    calls = []
+    for i in range(30):
+        n = int(rng.choice([1, 1, 1, 2, 5]))
+        l0 = int(rng.integers(0, N_LAYERS))
+        l1 = int(rng.integers(l0 + 1, N_LAYERS + 1))
+        t0 = int(rng.integers(0, 16 - n + 1))
+        calls.append((n, l0, l1, t0))
+    try:
+        outs = [m.forward(x[t0:t0 + n], l0, l1) for n, l0, l1, t0 in calls]   # queued, no sync between
+        refs = [ref.forward(x[t0:t0 + n], l0, l1) for n, l0, l1, t0 in calls]
+        torch.cuda.synchronize()
+        m.status()
+        ref.status()
+        for i, (a, b) in enumerate(zip(outs, refs)):
+            assert torch.equal(a, b), (i, calls[i])
+    finally:
+        ref.close()
