@@ -150,25 +150,53 @@ __device__ __forceinline__ void topk_exact(const double* c, int* ids) {
   }
 }
 
-// Top-6 of one token by one wavefront from its 256 scores (LDS), written as
-// ids (decreasing c, ties to the lower index) and weights s_i / sum_T s.
-__device__ __forceinline__ void route_token(const double* __restrict__ c, const double* __restrict__ s,
-                                            int* ids_out, float* w_out) {
+// Maximum of a 32-bit unsigned key over the wavefront, in every lane: rows of
+// 16 by DPP, then rows 0+1 and 2+3, then the two halves by the lane-swap
+// instructions (no read-back through a scalar register).
+__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_XOR1>(v));
+  v = max(v, dpp_u32<DPP_XOR2>(v));
+  v = max(v, dpp_u32<DPP_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_MIRROR>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // rows (0,0,2,2) / (1,1,3,3)
+  v = max((uint32_t)r[0], (uint32_t)r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // halves (lo,lo) / (hi,hi)
+  return max((uint32_t)h[0], (uint32_t)h[1]);
+}
+
+// Top-6 of one token by one wavefront from its 256 selection scores c: ids in
+// decreasing c, ties to the lower index (the same values in every lane).
+__device__ __forceinline__ void route_select(const double* __restrict__ c, int (&ids)[TOPK]) {
   const int lane = threadIdx.x & 63;
-  uint32_t k[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) k[j] = coarse_key(c[lane + 64 * j], lane + 64 * j);
+  uint32_t k0 = coarse_key(c[lane], lane), k1 = coarse_key(c[lane + 64], lane + 64);
+  uint32_t k2 = coarse_key(c[lane + 128], lane + 128), k3 = coarse_key(c[lane + 192], lane + 192);
+  // the lane's four keys in decreasing order (five compare-exchanges)
+  auto cx = [](uint32_t& hi, uint32_t& lo) {
+    const uint32_t a = max(hi, lo), b = min(hi, lo);
+    hi = a;
+    lo = b;
+  };
+  cx(k0, k1);
+  cx(k2, k3);
+  cx(k0, k2);
+  cx(k1, k3);
+  cx(k1, k2);
+  // seven rounds: the largest remaining key (keys are distinct: the index is
+  // in their low byte) leaves the head of its lane's list; every real key is
+  // above 0
   uint32_t picked[TOPK + 1];
 #pragma unroll
   for (int r = 0; r <= TOPK; ++r) {
-    const uint32_t m = wave_max_u32(max(max(k[0], k[1]), max(k[2], k[3])));
+    const uint32_t m = wave_max_all_u32(k0);
     picked[r] = m;
-    const int e = 255 - (int)(m & 0xFFu);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == e) k[j] = 0u;
+    const bool hit = k0 == m;
+    k0 = hit ? k1 : k0;
+    k1 = hit ? k2 : k1;
+    k2 = hit ? k3 : k2;
+    k3 = hit ? 0u : k3;
   }
-  int ids[TOPK];
+#pragma unroll
+  for (int r = 0; r <= TOPK; ++r) picked[r] = (uint32_t)__builtin_amdgcn_readfirstlane((int)picked[r]);
   if ((picked[TOPK - 1] >> 8) != (picked[TOPK] >> 8)) {
     // the k-th and (k+1)-th keys differ in their kept bits: the set is exact.
     // The keys order it exactly too, except inside runs of equal kept bits,
@@ -193,21 +221,50 @@ __device__ __forceinline__ void route_token(const double* __restrict__ c, const 
   } else {
     topk_exact(c, ids);
   }
+}
+
+// ids[0..6) to memory, by lanes 0..5.
+__device__ __forceinline__ void write_ids(const int (&ids)[TOPK], int* ids_out) {
+  const int lane = threadIdx.x & 63;
+  if (lane < TOPK) {
+    int id = ids[0];
+#pragma unroll
+    for (int r = 1; r < TOPK; ++r)
+      if (lane == r) id = ids[r];
+    ids_out[lane] = id;
+  }
+}
+
+// Weights of the picks ids[0..6): s_i / sum_T s in fp64, summed in pick
+// order; written as fp32 by lanes 0..5, which also return their weight.
+__device__ __forceinline__ float route_weights(const double* __restrict__ s, const int (&ids)[TOPK], float* w_out) {
+  const int lane = threadIdx.x & 63;
   double sv[TOPK], tot = 0.0;
 #pragma unroll
   for (int r = 0; r < TOPK; ++r) {
     sv[r] = s[ids[r]];
     tot += sv[r];
   }
+  float wv = 0.f;
   if (lane < TOPK) {
-    int id = ids[0];
     double v = sv[0];
 #pragma unroll
     for (int r = 1; r < TOPK; ++r)
-      if (lane == r) { id = ids[r]; v = sv[r]; }
-    ids_out[lane] = id;
-    w_out[lane] = (float)(v / tot);
+      if (lane == r) v = sv[r];
+    wv = (float)(v / tot);
+    w_out[lane] = wv;
   }
+  return wv;
+}
+
+// Top-6 of one token by one wavefront from its 256 scores: ids (decreasing c,
+// ties to the lower index) and weights s_i / sum_T s.
+__device__ __forceinline__ void route_token(const double* __restrict__ c, const double* __restrict__ s,
+                                            int* ids_out, float* w_out) {
+  int ids[TOPK];
+  route_select(c, ids);
+  write_ids(ids, ids_out);
+  route_weights(s, ids, w_out);
 }
 
 // ----------------------------------------------------------------- gate / up

@@ -363,20 +363,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         if (sync_or(!ok)) { rearm(); return; }
       }
       PHASE_MARK(5);
-      if (wave < nb) {
-        const double* zc = reinterpret_cast<const double*>(zbuf[wave]);
-        route_token(zc, zc + E, ids_l[t0 + wave], w_l[t0 + wave]);
+      if (wave == 0) {   // the selection; the publisher wave adds the weights below
+        int sel[TOPK];
+        route_select(reinterpret_cast<const double*>(zbuf[0]), sel);
+        write_ids(sel, ids_l[0]);
       }
       wg_sync();
     }
     PHASE_MARK(6);
-    if (w == 0 && A.trace_ids && wave == PUB_WAVE) {
-      for (int i = lane; i < n * TOPK; i += 64) {
-        const size_t o = (size_t)l * A.trace_cap * TOPK + i;
-        A.trace_ids[o] = ids_l[i / TOPK][i % TOPK];
-        A.trace_w[o] = w_l[i / TOPK][i % TOPK];
-      }
-    }
     // distinct experts of the call (for one token: its six picks, in pick order)
     const int D = (n == 1) ? TOPK : distinct_experts(ids_l, n, list, wave_tot);
     const int* dl = (n == 1) ? ids_l[0] : list;
@@ -435,6 +429,17 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       };
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
+      if (wave == PUB_WAVE) {   // routing weights, while this wave's loads fly (needed after the h exchange)
+        int sel[TOPK];
+#pragma unroll
+        for (int r = 0; r < TOPK; ++r) sel[r] = ids_l[0][r];
+        const float wv = route_weights(reinterpret_cast<const double*>(zbuf[0]) + E, sel, w_l[0]);
+        if (w == 0 && A.trace_ids && lane < TOPK) {
+          const size_t o = (size_t)l * A.trace_cap * TOPK + lane;
+          A.trace_ids[o] = ids_l[0][lane];
+          A.trace_w[o] = wv;
+        }
+      }
       if (wave < 4) {   // the shared row (its weights requested earlier) while the routed loads fly
         const int r = w * 4 + wave;
         for (int t = 0; t < n; ++t)
