@@ -199,7 +199,9 @@ class Synth:
     """Seeded synthetic weights for a stack of MoE layers.
 
     ``up_scale_mult`` maps a layer index to a power-of-two multiplier of the
-    routed experts' up-projection scales (exact in bf16).  ``bias_kind`` is
+    routed experts' up-projection scales (exact in bf16); ``up_scale_div``
+    divides them in every layer by a power of two (the fp16-intermediate pack
+    form).  ``bias_kind`` is
     "uniform" (U(-0.1, 0.1)) or "zipf" (b_e = -0.05 * 1.1 * ln r_e, r a seeded
     permutation of 1..E).
     """
@@ -208,6 +210,7 @@ class Synth:
     n_layers: int = 1
     up_scale_mult: Optional[Dict[int, int]] = None
     bias_kind: str = "uniform"
+    up_scale_div: int = 1
 
     # -- int4 code blocks
     def _codes(self, layer, tensor, experts, rows, k, device):
@@ -225,9 +228,10 @@ class Synth:
     def _up_shift(self, layer):
         mult = (self.up_scale_mult or {}).get(layer, 1)
         sh = int(mult).bit_length() - 1
-        if mult != 1 << sh:
-            raise ValueError("up-scale multiplier must be a power of two")
-        return sh
+        dsh = int(self.up_scale_div).bit_length() - 1
+        if mult != 1 << sh or self.up_scale_div != 1 << dsh:
+            raise ValueError("up-scale multiplier and divisor must be powers of two")
+        return sh - dsh
 
     def experts(self, layer: int, experts, device="cpu"):
         """Codes/scales of the given routed experts: dict of uint8/int16 tensors
@@ -245,7 +249,7 @@ class Synth:
         }
         sh = self._up_shift(layer)
         if sh:
-            out["up_s"] = out["up_s"] + (sh << 7)  # exponent field + sh: exact x 2^sh
+            out["up_s"] = out["up_s"] + (sh << 7)  # exponent field + sh: exact x 2^sh (scales are normal, positive)
         return out
 
     def shared(self, layer: int, device="cpu"):
@@ -342,9 +346,11 @@ def tokens(seed: int, idx, hidden: int = FLINT.hidden) -> np.ndarray:
     return np.stack([token(seed, int(t), hidden) for t in idx])
 
 
-def flint_stack(seed: int = 0, n_layers: int = N_LAYERS_FLINT, mult: int = 4096) -> Synth:
+def flint_stack(seed: int = 0, n_layers: int = N_LAYERS_FLINT, mult: int = 4096, up_div: int = 1) -> Synth:
     """The 47-layer stack workload: the last ten layers (37..46) multiply the
     routed up-projection scales by ``mult`` so SwiGLU intermediates reach the
-    1e5 range the pages report for the top layers."""
+    1e5 range the pages report for the top layers.  ``up_div`` > 1 gives the
+    fp16-intermediate pack form of the same weights (routed up scales divided
+    by it in every layer)."""
     top = {l: mult for l in range(max(0, n_layers - 10), n_layers)} if n_layers == N_LAYERS_FLINT else {}
-    return Synth(FLINT, seed, n_layers, up_scale_mult=top)
+    return Synth(FLINT, seed, n_layers, up_scale_mult=top, up_scale_div=up_div)

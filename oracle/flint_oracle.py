@@ -208,6 +208,48 @@ def moe_block(a, src, layer: int, shape, forced=None) -> BlockResult:
     return BlockResult(delta=delta, route=r, max_abs_h=hmax)
 
 
+# ------------------------------------------------------------------ fp16 intermediates
+# TandemLLM "21 Flint", 21.2: SwiGLU outputs of the routed experts reach about
+# 2.6e5 in the top layers, past fp16, so the published packs store each routed
+# expert's up projection divided by a power of two (expert_interm_div, 128
+# there) and the engine multiplies the routing weights back.  Readings: the
+# SwiGLU output of every expert, routed and shared, is rounded to fp16 before
+# its down projection (round to nearest even, +-inf past the largest finite
+# value); only the routed up projections are divided; gate and up are as in
+# moe_block.
+
+
+def round_to_fp16(x) -> np.ndarray:
+    """fp64 -> the nearest fp16 value (ties to even; +-inf beyond the finite
+    range), returned as fp64."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def moe_block_fp16_interm(a, src, layer: int, shape, interm_div: int, forced=None) -> BlockResult:
+    """moe_block in the fp16-intermediate form.  ``src`` holds the pack's
+    weights: every routed expert's up projection already divided by
+    ``interm_div``.  max_abs_h is over the fp16 SwiGLU outputs."""
+    r = route(a, src.router(layer), src.bias(layer), shape.top_k, forced)
+    ex = src.experts(layer, [int(e) for e in r.ids])
+    ex = {k: np.asarray(v) for k, v in ex.items()}
+    a = np.asarray(a, dtype=np.float64)
+    delta = np.zeros(shape.hidden, dtype=np.float64)
+    hmax = 0.0
+    for i in range(len(r.ids)):
+        wg, wu, wd = _dense(ex, i, shape.group)
+        h = round_to_fp16(silu(wg @ a) * (wu @ a))
+        delta += (interm_div * r.weights[i]) * (wd @ h)
+        hmax = max(hmax, float(np.max(np.abs(h))))
+    sh = {k: np.asarray(v) for k, v in src.shared(layer).items()}
+    g = dequant(sh["gate"], sh["gate_s"], shape.group) @ a
+    u = dequant(sh["up"], sh["up_s"], shape.group) @ a
+    h_sh = round_to_fp16(silu(g) * u)
+    delta += dequant(sh["down"], sh["down_s"], shape.group) @ h_sh
+    hmax = max(hmax, float(np.max(np.abs(h_sh))))
+    return BlockResult(delta=delta, route=r, max_abs_h=hmax)
+
+
 def block_input(x, shape) -> np.ndarray:
     """RMS-normalise the fp32 residual and round to bf16 (real shape)."""
     a = rms_normalise(np.asarray(x, dtype=np.float32).astype(np.float64))
