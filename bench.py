@@ -210,14 +210,16 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
-def build_stack_model(dev):
+def build_stack_model(dev, interm_div=0):
+    """The 47-layer stack on ``dev``; interm_div > 0 gives the fp16-intermediate
+    pack form of the same weights (routed up scales divided by it)."""
     import torch
     import flintgen as fg
     import int4_expert_ffn_amd as F
-    synth = fg.flint_stack(0, N_LAYERS)
+    synth = fg.flint_stack(0, N_LAYERS, up_div=interm_div or 1)
     layers = [synth.layer(l, dev) for l in range(N_LAYERS)]
     torch.cuda.synchronize()
-    model = F.FlintMoE(layers)
+    model = F.FlintMoE(layers, interm_div=interm_div)
     del layers
     torch.cuda.empty_cache()
     return model
@@ -422,22 +424,24 @@ def cpu_baseline_head(seconds_budget=20.0):
             "sample": f"one token, head rows 0..{rows - 1} in blocks of 4,096 ({spent:.1f} s of oracle time)"}
 
 
-def cpu_baseline(seconds_budget=20.0):
+def cpu_baseline(seconds_budget=20.0, interm_div=0):
     """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
     many of the 47 layers as fit the budget; scaled to tokens/s for the whole
-    stack."""
+    stack.  interm_div > 0: the oracle's fp16-intermediate form on the pack
+    weights."""
     import flintgen as fg
     from oracle import flint_oracle as O
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle_sources import SynthSource
-    synth = fg.flint_stack(0, N_LAYERS)
+    synth = fg.flint_stack(0, N_LAYERS, up_div=interm_div or 1)
     src = SynthSource(synth)
     x = fg.token(0, 0)
     t0 = time.perf_counter()
     layers = 0
     for l in range(N_LAYERS):
         a = O.block_input(x, fg.FLINT)
-        res = O.moe_block(a, src, l, fg.FLINT)
+        res = (O.moe_block_fp16_interm(a, src, l, fg.FLINT, interm_div) if interm_div
+               else O.moe_block(a, src, l, fg.FLINT))
         x = (x.astype(np.float64) + res.delta).astype(np.float32)
         layers += 1
         if time.perf_counter() - t0 > seconds_budget:
@@ -475,6 +479,9 @@ def main():
     ap.add_argument("--cost-table", action="store_true",
                     help="time one 47-layer call for n = 1..16 tokens (verify-block cost table)")
     ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
+    ap.add_argument("--interm-div", type=int, default=0,
+                    help="time the fp16-intermediate form instead: the same stack with routed up projections "
+                         "divided by this power of two (128 in the published packs)")
     args = ap.parse_args()
     if args.counters_summary:
         summarize_counters(*args.counters_summary, commands=args.command, which=args.counters_kernel)
@@ -508,7 +515,7 @@ def main():
         return
 
     t_setup = time.perf_counter()
-    model = build_stack_model(dev)
+    model = build_stack_model(dev, args.interm_div)
     pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
     out = torch.empty((1, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -549,9 +556,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xbf16->fp32",
+        "dtype": "int4xbf16->fp32" + (", fp16 SwiGLU outputs" if args.interm_div else ""),
         "data": "synthetic (seeded int4 weights, bf16 scales, N(0,1) tokens)",
-        "config": {"workload": "47-layer Flint MoE block stack, batch 1 decode", "layers": N_LAYERS,
+        "config": {"workload": "47-layer Flint MoE block stack, batch 1 decode"
+                               + (f", fp16 intermediates (routed up / {args.interm_div})" if args.interm_div else ""),
+                   "layers": N_LAYERS,
                    "hidden": H, "experts": E, "top_k": K, "expert_size": I, "shared_size": IS,
                    "group": G, "tokens_per_step": 1, "token_pool": 64,
                    "algorithmic_bytes_per_token": TOKEN_BYTES},
@@ -564,8 +573,11 @@ def main():
                      "launch_us_p90": round(float(np.percentile(durs, 90)) * 1e6, 2)},
         "setup_s": round(setup_s, 1),
     }
+    if args.interm_div:
+        res["config"]["interm_div"] = args.interm_div
+        res["roofline"]["traffic"] = None   # the counters were taken on the fp32 form
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds, args.interm_div)
     print(json.dumps(res), flush=True)
 
 

@@ -91,6 +91,22 @@ typedef struct {
  * On failure *out is set to NULL and nothing is leaked. */
 int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* out);
 
+/* Create a handle for weights in the fp16-intermediate pack form (TandemLLM
+ * "21 Flint", 21.2: the packs divide each routed expert's up projection by a
+ * power of two, expert_interm_div, so that the SwiGLU outputs of the top
+ * layers fit fp16, and the engine multiplies the routing weights back).
+ * `weights` as for flint_moe_create, with every routed expert's up-projection
+ * scales already divided by interm_div (a power of two in [1, 32768]; 128 in
+ * the pages' packs); the shared expert is not divided.  forward on such a
+ * handle rounds the SwiGLU output of every expert (routed and shared) to fp16,
+ * nearest even (overflow gives inf), before its down projection, and scales
+ * the routed weights by interm_div in the combine.  It is implemented for
+ * single-token calls (n_tokens == 1) on GPUs that run the persistent decode
+ * kernel; other calls return FLINT_ERR_UNSUPPORTED.  interm_div = 0 is
+ * flint_moe_create. */
+int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, int interm_div,
+                                 flint_moe_t* out);
+
 /* Apply layers [layer_begin, layer_end) to n_tokens independent fp32 residual
  * rows x [n_tokens][H] (device), writing out [n_tokens][H] (device).  out == x
  * is allowed; partial overlap is not.  1 <= n_tokens <= FLINT_MAX_TOKENS and

@@ -33,7 +33,7 @@ FLINT_DENSE_MLP_SIZE = 6144
 FLINT_VOCAB = 150144
 FLINT_DENSE_MAX_TOKENS = 16
 
-EXPORTED = ("flint_moe_create", "flint_moe_forward", "flint_moe_set_trace", "flint_moe_status",
+EXPORTED = ("flint_moe_create", "flint_moe_create_fp16_interm", "flint_moe_forward", "flint_moe_set_trace", "flint_moe_status",
             "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward", "flint_head_forward")
 
 
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         vp, ci = ctypes.c_void_p, ctypes.c_int
         L.flint_moe_create.argtypes = [ctypes.POINTER(flint_moe_layer), ci, ctypes.POINTER(vp)]
         L.flint_moe_create.restype = ci
+        L.flint_moe_create_fp16_interm.argtypes = [ctypes.POINTER(flint_moe_layer), ci, ci, ctypes.POINTER(vp)]
+        L.flint_moe_create_fp16_interm.restype = ci
         L.flint_moe_forward.argtypes = [vp, vp, ci, ci, ci, vp, vp]
         L.flint_moe_forward.restype = ci
         L.flint_moe_set_trace.argtypes = [vp, vp, vp, ci]
@@ -108,12 +110,23 @@ def layer_struct(d) -> flint_moe_layer:
                            q("sh_down", "sh_down_s"))
 
 
+def _layer_array(layers):
+    return (flint_moe_layer * len(layers))(*[l if isinstance(l, flint_moe_layer) else layer_struct(l)
+                                             for l in layers])
+
+
 def flint_moe_create(layers) -> int:
     """layers: sequence of per-layer mappings (see layer_struct) or flint_moe_layer."""
-    arr = (flint_moe_layer * len(layers))(*[l if isinstance(l, flint_moe_layer) else layer_struct(l)
-                                            for l in layers])
     h = ctypes.c_void_p()
-    _check(lib().flint_moe_create(arr, len(layers), ctypes.byref(h)))
+    _check(lib().flint_moe_create(_layer_array(layers), len(layers), ctypes.byref(h)))
+    return h.value
+
+
+def flint_moe_create_fp16_interm(layers, interm_div) -> int:
+    """Handle for weights whose routed up projections are divided by
+    ``interm_div``; SwiGLU outputs are rounded to fp16 (single-token calls)."""
+    h = ctypes.c_void_p()
+    _check(lib().flint_moe_create_fp16_interm(_layer_array(layers), len(layers), interm_div, ctypes.byref(h)))
     return h.value
 
 
@@ -161,11 +174,13 @@ def _stream(stream):
 
 
 class FlintMoE:
-    """Owning wrapper: ``FlintMoE(layers)``, ``forward(x, l0, l1, out)``."""
+    """Owning wrapper: ``FlintMoE(layers)``, ``forward(x, l0, l1, out)``.
+    ``interm_div`` > 0 selects the fp16-intermediate form (see
+    flint_moe_create_fp16_interm)."""
 
-    def __init__(self, layers):
+    def __init__(self, layers, interm_div=0):
         self.n_layers = len(layers)
-        self.h = flint_moe_create(layers)
+        self.h = flint_moe_create_fp16_interm(layers, interm_div) if interm_div else flint_moe_create(layers)
 
     def forward(self, x, layer_begin=0, layer_end=None, out=None, stream=None):
         import torch

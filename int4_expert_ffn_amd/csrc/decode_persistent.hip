@@ -20,6 +20,8 @@
 //
 // The arithmetic is the same code as the per-layer kernels (decode_common.h),
 // so both launch modes give bitwise-identical results.
+#include <hip/hip_fp16.h>
+
 #include "decode_common.h"
 #include "decode_persistent.h"
 
@@ -132,11 +134,12 @@ __device__ __forceinline__ bool has_empty(uint4 v) {
 }
 
 // Wait until values src[0..nvals) (nvals a multiple of 4) are all written;
-// store value j in dst[pos(j)].  Thread i polls the 16-byte groups i + NTHR k,
-// k < K.  Returns false on timeout (the device error word is then set).
-template <int K, typename Pos, int NTHR = NT>
-__device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, uint32_t* dst, int* err, Pos pos,
-                                              int tid, int dbg_layer, int dbg_id, GtsLds gts_lds) {
+// hand value j to sink(j, value).  Thread i polls the 16-byte groups
+// i + NTHR k, k < K.  Returns false on timeout (the device error word is then
+// set).
+template <int K, typename Sink, int NTHR = NT>
+__device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, int* err, Sink sink, int tid,
+                                              int dbg_layer, int dbg_id, GtsLds gts_lds) {
   GATHER_PROBE(0, wall_clock64());
   unsigned long long iters = 0;
   const int ngroups = nvals >> 2;
@@ -174,10 +177,10 @@ __device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, ui
   for (int k = 0; k < K; ++k) {
     const int j = tid + NTHR * k;
     if (j < ngroups) {
-      dst[pos(4 * j)] = v[k].x;
-      dst[pos(4 * j + 1)] = v[k].y;
-      dst[pos(4 * j + 2)] = v[k].z;
-      dst[pos(4 * j + 3)] = v[k].w;
+      sink(4 * j, v[k].x);
+      sink(4 * j + 1, v[k].y);
+      sink(4 * j + 2, v[k].z);
+      sink(4 * j + 3, v[k].w);
     }
   }
   return true;
@@ -215,6 +218,29 @@ struct HPosWG {
   }
 };
 
+// Where the single-token gathers put their values in LDS.
+struct StoreAt {   // value j -> dst[j]
+  uint32_t* dst;
+  __device__ void operator()(int j, uint32_t v) const { dst[j] = v; }
+};
+struct StoreH {    // fp32 h word j (workgroup-major) -> its transposed position
+  uint32_t* dst;
+  __device__ void operator()(int j, uint32_t v) const { dst[HPosWG()(j)] = v; }
+};
+struct StoreH16 {  // word j = fp16 h values 2 j (low half) and 2 j + 1 -> fp32 at their positions
+  float* dst;
+  __device__ void operator()(int j, uint32_t v) const {
+    dst[HPosWG()(2 * j)] = __half2float(__ushort_as_half((unsigned short)(v & 0xFFFFu)));
+    dst[HPosWG()(2 * j + 1)] = __half2float(__ushort_as_half((unsigned short)(v >> 16)));
+  }
+};
+
+// fp16 bits of a value that is already exactly an fp16 value (or inf); NaN
+// becomes the canonical quiet NaN, so a packed pair is never EMPTY_WORD.
+__device__ __forceinline__ uint32_t fp16_bits(float v) {
+  return (v != v) ? 0x7E00u : (uint32_t)__half_as_ushort(__float2half_rn(v));
+}
+
 // Role split inside a workgroup: on GFX9 a wavefront's memory counter retires
 // loads and stores in issue order, so a poll issued after a store waits for
 // that store's acknowledgement.  The last wave publishes each exchange (from
@@ -222,6 +248,12 @@ struct HPosWG {
 constexpr int PUB_WAVE = NWAVES - 1;
 constexpr int NPOLL = NT - 64;   // polling threads: waves 0 .. NWAVES-2
 
+// F16H: the fp16-intermediate form (TandemLLM "21 Flint", 21.2: packs store
+// each routed expert's up projection divided by a power of two so SwiGLU
+// outputs fit fp16, and the engine multiplies the routing weights back).
+// Every expert's SwiGLU output is rounded to fp16; the h exchange carries two
+// values per word; routed weights are scaled by A.interm_mult in the combine.
+template <bool F16H>
 __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
   __shared__ __align__(16) uint4 a_lds[DECODE_MAX_TOKENS][256];
   __shared__ float asum_lds[DECODE_MAX_TOKENS][64];
@@ -274,16 +306,19 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     return r;
   };
   // Re-arm this workgroup's slots of the other parity for every layer (its x
-  // rows 8 w .. 8 w + 7 and h words 16 w .. 16 w + 15): the next call writes
-  // them.  Runs on every way out of the kernel.
+  // rows 8 w .. 8 w + 7 and h words 16 w .. 16 w + 15, or 8 w .. 8 w + 7 with
+  // two fp16 values per word): the next call writes them.  Runs on every way
+  // out of the kernel.
+  constexpr int HWORDS_WG = F16H ? 8 : 16;   // h words per workgroup
+  constexpr int RQ = 2 + HWORDS_WG / 4;      // 16-byte pieces re-armed per layer
   const int other = A.parity ^ 1;
   auto rearm = [&]() {
     if (wave != PUB_WAVE) return;
     const uint4 empty = make_uint4(EMPTY_WORD, EMPTY_WORD, EMPTY_WORD, EMPTY_WORD);
-    for (int i = lane; i < 6 * A.n_layers; i += 64) {
-      const int lc = i / 6, q = i % 6;
+    for (int i = lane; i < RQ * A.n_layers; i += 64) {
+      const int lc = i / RQ, q = i % RQ;
       const size_t slot = (size_t)other * A.n_layers + lc;
-      uint32_t* p = q < 2 ? A.vx + slot * H + 8 * w + 4 * q : A.vh + slot * HW + 16 * w + 4 * (q - 2);
+      uint32_t* p = q < 2 ? A.vx + slot * H + 8 * w + 4 * q : A.vh + slot * HW + HWORDS_WG * w + 4 * (q - 2);
       *reinterpret_cast<uint4*>(p) = empty;
     }
   };
@@ -306,9 +341,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       if (l == A.l0) {
         if (tid < H / 4) reinterpret_cast<float4*>(xstage)[tid] = reinterpret_cast<const float4*>(A.x + (size_t)t * H)[tid];
       } else if (poller) {
-        ok = gather_values<(H / 4 + NPOLL - 1) / NPOLL, Identity, NPOLL>(
-            A.vx + ((size_t)A.parity * A.n_layers + (l - 1)) * H, H, reinterpret_cast<uint32_t*>(xstage), A.err,
-            Identity(), tid, l, 0, gts_lds);
+        ok = gather_values<(H / 4 + NPOLL - 1) / NPOLL, StoreAt, NPOLL>(
+            A.vx + ((size_t)A.parity * A.n_layers + (l - 1)) * H, H, A.err,
+            StoreAt{reinterpret_cast<uint32_t*>(xstage)}, tid, l, 0, gts_lds);
       }
       if (sync_or(!ok)) { rearm(); return; }
       if (t == 0) PHASE_MARK(1);
@@ -409,7 +444,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       // lanes write consecutive words (whole 32-byte pieces)
       auto emit = [&](int j, int word, float hv) {
         if (lane == 0) {
-          hloc[j] = hv;
+          hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
           hloc_idx[j] = word;
         }
       };
@@ -455,12 +490,24 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     wg_sync();
     PUB_MARK(13);
     if (wave == PUB_WAVE) {
-      const int cnt = 4 + 2 * D;   // one value per task (one token)
-      for (int k = lane; k < cnt; k += 64) {
-        const int word = hloc_idx[k];
-        // one 128-byte run per workgroup (the h words of its tasks, in task order)
-        if (word >= 0 && word < n * HW) publish_value(vh_l + 16 * w + k, hloc[k]);
-        else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int cnt = 4 + 2 * D;   // one value per task (one token): 16
+      if constexpr (F16H) {
+        // one 32-byte run per workgroup: values 2 k and 2 k + 1 in word k
+        if (lane < cnt / 2) {
+          const int w0 = hloc_idx[2 * lane], w1 = hloc_idx[2 * lane + 1];
+          if (w0 >= 0 && w0 < HW && w1 >= 0 && w1 < HW)
+            __hip_atomic_store(vh_l + 8 * w + lane, fp16_bits(hloc[2 * lane]) | (fp16_bits(hloc[2 * lane + 1]) << 16),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        for (int k = lane; k < cnt; k += 64) {
+          const int word = hloc_idx[k];
+          // one 64-byte run per workgroup (the h values of its tasks, in task order)
+          if (word >= 0 && word < n * HW) publish_value(vh_l + 16 * w + k, hloc[k]);
+          else __hip_atomic_store(A.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     PUB_MARK(14);
@@ -472,9 +519,14 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       uint32_t sa = sa0, sb = sb0;
       if (t > 0) load_down_row(L, ids_l[t], row, ca, sa, cb, sb);
       bool ok = true;
-      if (poller)
-        ok = gather_values<(HW / 4 + NPOLL - 1) / NPOLL, HPosWG, NPOLL>(
-            vh_l, HW, reinterpret_cast<uint32_t*>(hbuf), A.err, HPosWG(), tid, l, 2, gts_lds);
+      if (poller) {
+        if constexpr (F16H)
+          ok = gather_values<(HW / 8 + NPOLL - 1) / NPOLL, StoreH16, NPOLL>(vh_l, HW / 2, A.err, StoreH16{hbuf}, tid,
+                                                                           l, 2, gts_lds);
+        else
+          ok = gather_values<(HW / 4 + NPOLL - 1) / NPOLL, StoreH, NPOLL>(
+              vh_l, HW, A.err, StoreH{reinterpret_cast<uint32_t*>(hbuf)}, tid, l, 2, gts_lds);
+      }
       if (sync_or(!ok)) { rearm(); return; }
       if (t == 0) PHASE_MARK(9);
       const int sub = lane & 15;
@@ -483,7 +535,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
                            : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
       };
-      const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l[t], xown[t][wave]);
+      float wsc[TOPK];   // routed weights, times the pack's divisor in the fp16 form
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) wsc[i] = F16H ? w_l[t][i] * A.interm_mult : w_l[t][i];
+      const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, wsc, xown[t][wave]);
       if (lane == 0) xnew[t][wave] = v;
       wg_sync();   // hbuf is rewritten by the next token
     }
@@ -955,7 +1010,8 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   // power of two at or above n: the statically sized kernel leaves K - n
   // groups idle, the exact-range kernel uses every workgroup but runs about
   // a quarter slower per row; measured, the exact ranges win when n < 0.7 K.
-  const void* k = reinterpret_cast<const void*>(k_decode_persistent);
+  const void* k = a.interm_mult != 0.f ? reinterpret_cast<const void*>(k_decode_persistent<true>)
+                                       : reinterpret_cast<const void*>(k_decode_persistent<false>);
   const int n = a.n;
   const int K = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
   const bool exact = 10 * n < 7 * K;

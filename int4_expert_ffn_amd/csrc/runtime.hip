@@ -77,6 +77,7 @@ struct flint_moe {
   uint32_t* vx = nullptr;   // single-token exchange slots, two call parities
   uint32_t* vh = nullptr;
   int parity = 0;           // parity of the next single-token call
+  int interm_div = 0;       // 0: fp32 SwiGLU outputs; else the fp16-intermediate form with this divisor
 };
 
 static void release(flint_moe* h) {
@@ -117,8 +118,14 @@ extern "C" {
 const char* flint_moe_last_error(void) { return g_last_error.c_str(); }
 
 int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* out) {
+  return flint_moe_create_fp16_interm(weights, n_layers, 0, out);
+}
+
+int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, int interm_div, flint_moe_t* out) {
   if (!out) return fail(FLINT_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
+  if (interm_div != 0 && (interm_div < 1 || interm_div > (1 << 15) || (interm_div & (interm_div - 1)) != 0))
+    return fail(FLINT_ERR_INVALID_ARG, "interm_div = %d is not a power of two in [1, 32768]", interm_div);
   if (!weights) return fail(FLINT_ERR_INVALID_ARG, "weights is NULL");
   if (n_layers < 1 || n_layers > FLINT_MAX_LAYERS)
     return fail(FLINT_ERR_INVALID_ARG, "n_layers = %d outside [1, %d]", n_layers, FLINT_MAX_LAYERS);
@@ -134,6 +141,7 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { int r = fail_hip(e, "hipGetDevice"); h->device = -1; release(h); return r; }
   h->n_layers = n_layers;
+  h->interm_div = interm_div;
   LayerSizes sz;
   const size_t per_layer = sz.total();
   int rc = checked_malloc((void**)&h->arena, per_layer * n_layers, "weights");
@@ -226,6 +234,9 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
   if (((uintptr_t)x | (uintptr_t)out) & 15) return fail(FLINT_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   if (n_tokens < 1 || n_tokens > FLINT_MAX_TOKENS)
     return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_MAX_TOKENS);
+  if (h->interm_div && !(n_tokens == 1 && h->persistent))
+    return fail(FLINT_ERR_UNSUPPORTED, "fp16 intermediates are implemented for single-token calls on the "
+                                       "persistent decode path (n_tokens = %d)", n_tokens);
   if (layer_begin < 0 || layer_end > h->n_layers || layer_begin >= layer_end)
     return fail(FLINT_ERR_INVALID_ARG, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
                 h->n_layers);
@@ -267,6 +278,7 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
     a.vh = h->vh;
     a.n_layers = h->n_layers;
     a.parity = h->parity;
+    a.interm_mult = (float)h->interm_div;
     e = launch_decode_persistent(a, s);
     if (e != hipSuccess) return fail_hip(e, "persistent decode launch");
     // a single-token call writes the slots of its parity and re-arms the

@@ -55,6 +55,12 @@ def test_create_rejects_bad_arguments_before_any_hip_call():
     assert lib.flint_moe_create(layer, 1, ctypes.byref(h)) == F.FLINT_ERR_INVALID_ARG   # null tensors
     assert "NULL" in F.flint_moe_last_error()
     assert lib.flint_moe_create(layer, 1, None) == F.FLINT_ERR_INVALID_ARG
+    for div in (-128, 3, 96, 1 << 16):   # the fp16-intermediate divisor: a power of two in [1, 32768]
+        h = ctypes.c_void_p(1234)
+        assert lib.flint_moe_create_fp16_interm(layer, 1, div, ctypes.byref(h)) == F.FLINT_ERR_INVALID_ARG
+        assert h.value is None
+        assert "interm_div" in F.flint_moe_last_error()
+    assert lib.flint_moe_create_fp16_interm(layer, 1, 128, ctypes.byref(h)) == F.FLINT_ERR_INVALID_ARG  # null tensors
 
 
 def test_null_handle_calls():
