@@ -41,10 +41,18 @@ LAYER_BYTES = ROUTER_BYTES + K * EXPERT_BYTES + SHARED_BYTES   # 14,025,728
 TOKEN_BYTES = N_LAYERS * LAYER_BYTES                           # 659,209,216
 
 
-def kernel_source_hash():
+# Sources each profiled kernel is compiled from: a counter summary holds only
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "decode": ("decode_persistent.hip", "decode_persistent.h", "decode_common.h", "decode.h", "flint_device.h"),
+    "head": ("dense.hip", "dense.h", "flint_device.h"),
+}
+
+
+def kernel_source_hash(which="decode"):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_expert_ffn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KERNEL_SOURCES[which]):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -54,7 +62,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stack47_traffic.txt")
 DECODE_KERNEL = "k_decode_persistent"
 
 
-def traffic_from_profiles(path=None):
+def traffic_from_profiles(path=None, which="decode"):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
     summary (the decode kernel by default), if it was taken on the current
     kernel sources; else None."""
@@ -67,7 +75,7 @@ def traffic_from_profiles(path=None):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(which):
         return None
     return int(vals["hbm_bytes_per_launch"])
 
@@ -126,7 +134,8 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, com
         title,
         "# from rocprofv3 --pmc, one counter per run, calibrated with a plain 1 GiB device copy",
         f"kernel: {kname}",
-        f"kernel_source_hash: {kernel_source_hash()}",
+        f"kernel_source_hash: {kernel_source_hash(which)}",
+        f"kernel_sources: {' '.join(KERNEL_SOURCES[which])}",
         f"dispatches_fetch: {len(f)}",
         f"fetch_kib_per_dispatch_median: {f_kib:.1f}",
         f"write_kib_per_dispatch_median: {w_kib:.1f}",
@@ -359,7 +368,7 @@ def bench_head_dense(args):
         "config": {"workload": "output head 150,144 x 2,048 int4 and dense SwiGLU MLP 2,048 -> 6,144 -> 2,048, "
                                "decode", "head_bytes": head_bytes, "dense_mlp_bytes": dense_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profiles(HEAD_TRAFFIC_FILE),
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_from_profiles(HEAD_TRAFFIC_FILE, "head"),
                      "kernel": "k_rows_mfma (head, one launch)"},
         "head_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_head.items()},
         "dense_mlp_us": {str(n): [round(v * 1e6, 2) for v in r] for n, r in res_dense.items()},
