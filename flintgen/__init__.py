@@ -46,6 +46,8 @@ T_ROUTER, T_BIAS = 12, 13
 T_DENSE_GATE, T_DENSE_UP, T_DENSE_DOWN = 14, 15, 16
 T_DENSE_GATE_S, T_DENSE_UP_S, T_DENSE_DOWN_S = 17, 18, 19
 T_HEAD, T_HEAD_S = 20, 21
+# decode attention inputs
+T_ATT_Q, T_ATT_K, T_ATT_V, T_ATT_SINK = 22, 23, 24, 25
 TOKEN_BASE = 1_000_000
 DENSE_MLP_SIZE = 6144   # config table row "Dense MLP size" (layers 0 and 1)
 VOCAB = 150144          # config table row "Vocabulary": rows of the output head
@@ -354,3 +356,37 @@ def flint_stack(seed: int = 0, n_layers: int = N_LAYERS_FLINT, mult: int = 4096,
     by it in every layer)."""
     top = {l: mult for l in range(max(0, n_layers - 10), n_layers)} if n_layers == N_LAYERS_FLINT else {}
     return Synth(FLINT, seed, n_layers, up_scale_mult=top, up_scale_div=up_div)
+
+
+# ---------------------------------------------------------------- decode attention
+# Attention of one layer (TandemLLM "21 Flint", 21.1 table rows "attention",
+# "sliding layers", "full layers"; How to Run Flint Locally, "Sinks and the
+# 513-token window"): 32 query heads, 4 KV heads of 128, a 513-position window
+# held in a ring of 640 rows on window layers, every position on full layers,
+# one learned sink logit per query head (the checkpoint's offsets run from -9.0
+# to 12.4).
+ATT_Q_HEADS, ATT_KV_HEADS, ATT_HEAD_DIM = 32, 4, 128
+ATT_WINDOW, ATT_RING = 513, 640
+
+
+def attn_queries(seed: int, layer: int, n_tokens: int) -> np.ndarray:
+    """q [n][32][128] fp32, N(0, 1) per element (as after the per-head RMS norm)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, layer, T_ATT_Q, n_tokens]))
+    return rng.standard_normal((n_tokens, ATT_Q_HEADS, ATT_HEAD_DIM)).astype(np.float32)
+
+
+def attn_cache(seed: int, layer: int, rows: int):
+    """k, v caches [rows][4][128] as bf16 bit patterns (int16), N(0, 1) values."""
+    out = []
+    for t in (T_ATT_K, T_ATT_V):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, layer, t, rows]))
+        x = torch.from_numpy(rng.standard_normal((rows, ATT_KV_HEADS, ATT_HEAD_DIM), dtype=np.float32))
+        out.append(x.to(torch.bfloat16).view(torch.int16).numpy())
+    return out[0], out[1]
+
+
+def attn_sinks(seed: int, layer: int) -> np.ndarray:
+    """One sink logit per query head: U(-9.0, 12.4) rounded to bf16, as fp32."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, layer, T_ATT_SINK, 0]))
+    x = torch.from_numpy(rng.uniform(-9.0, 12.4, ATT_Q_HEADS).astype(np.float32))
+    return x.to(torch.bfloat16).float().numpy()

@@ -346,3 +346,40 @@ def bytes_per_token_layer(shape, n_tokens_experts: int = None) -> int:
     shared = 2 * q4(shape.shared_size, shape.hidden) + q4(shape.hidden, shape.shared_size)
     router = shape.n_experts * shape.hidden * 2 + shape.n_experts * 4
     return router + e * expert + shared
+
+
+# ------------------------------------------------------------------ decode attention
+# One layer's attention for one query token (How to Run Flint Locally, "Sinks
+# and the 513-token window": a window layer sees the current token and the 512
+# before it; a sink is one more softmax slot with a fixed logit, the head's
+# learned offset, and no value vector.  TandemLLM "21 Flint", 21.1 table: 32
+# query heads, 4 KV heads of 128; window layers keep a ring of 640 rows; full
+# layers see every position).  Readings: query head h reads KV head
+# h // (32 / 4) (consecutive query heads share a KV head); scores are
+# q . k / sqrt(128); the query, keys and values arrive already normed and
+# rotated (this step does not include the projections, the QK norm or RoPE).
+
+
+def attention_decode(q, k, v, sinks, pos: int, window: int, n_kv: int = 4) -> np.ndarray:
+    """q [Hq][D] query values; k, v [R][n_kv][D] cache values with position p at
+    row p % R; sinks [Hq]; the token at ``pos`` sees positions
+    max(0, pos - window + 1) .. pos (window = 0: all of 0 .. pos).  Returns
+    out [Hq][D] in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, d = q.shape
+    ring = k.shape[0]
+    first = max(0, pos - window + 1) if window else 0
+    if pos - first + 1 > ring:
+        raise ValueError("the positions a token sees must fit the cache rows")
+    rows = np.arange(first, pos + 1) % ring
+    out = np.zeros((n_q, d))
+    group = n_q // n_kv
+    for h in range(n_q):
+        g = h // group
+        logits = np.concatenate([(k[rows, g, :] @ q[h]) / np.sqrt(d), [float(sinks[h])]])
+        e = np.exp(logits - logits.max())
+        p = e / e.sum()
+        out[h] = p[:-1] @ v[rows, g, :]
+    return out
