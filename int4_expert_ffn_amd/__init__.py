@@ -33,8 +33,16 @@ FLINT_DENSE_MLP_SIZE = 6144
 FLINT_VOCAB = 150144
 FLINT_DENSE_MAX_TOKENS = 16
 
-EXPORTED = ("flint_moe_create", "flint_moe_create_fp16_interm", "flint_moe_forward", "flint_moe_set_trace", "flint_moe_status",
-            "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward", "flint_head_forward")
+FLINT_ATT_Q_HEADS = 32
+FLINT_ATT_KV_HEADS = 4
+FLINT_ATT_HEAD_DIM = 128
+FLINT_ATT_WINDOW = 513
+FLINT_ATT_RING = 640
+FLINT_ATT_MAX_TOKENS = 16
+
+EXPORTED = ("flint_moe_create", "flint_moe_create_fp16_interm", "flint_moe_forward", "flint_moe_set_trace",
+            "flint_moe_status", "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward",
+            "flint_head_forward", "flint_attn_workspace_bytes", "flint_attn_decode")
 
 
 class flint_q4(ctypes.Structure):
@@ -82,6 +90,11 @@ def lib() -> ctypes.CDLL:
         L.flint_dense_mlp_forward.restype = ci
         L.flint_head_forward.argtypes = [flint_q4, ci, vp, ci, vp, vp]
         L.flint_head_forward.restype = ci
+        L.flint_attn_workspace_bytes.argtypes = [ci, ci]
+        L.flint_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.flint_attn_decode.argtypes = [vp, vp, vp, ci, vp, ctypes.POINTER(ctypes.c_int32), ci, ci, vp, vp,
+                                        ctypes.c_size_t, vp]
+        L.flint_attn_decode.restype = ci
         _lib = L
     return _lib
 
@@ -163,6 +176,18 @@ def flint_dense_mlp_forward(gate, up, down, inter, x, n_tokens, h, out, stream=N
 
 def flint_head_forward(head, rows, x, n_tokens, logits, stream=None) -> None:
     _check(lib().flint_head_forward(head, rows, _ptr(x), n_tokens, _ptr(logits), _stream(stream)))
+
+
+def flint_attn_workspace_bytes(n_tokens, max_seen) -> int:
+    return lib().flint_attn_workspace_bytes(n_tokens, max_seen)
+
+
+def flint_attn_decode(q, k, v, ring_rows, sinks, pos, n_tokens, window, out, workspace, workspace_bytes,
+                      stream=None) -> None:
+    """pos: host sequence of n_tokens positions; the rest device tensors or addresses."""
+    p = (ctypes.c_int32 * n_tokens)(*[int(x) for x in pos])
+    _check(lib().flint_attn_decode(_ptr(q), _ptr(k), _ptr(v), ring_rows, _ptr(sinks), p, n_tokens, window, _ptr(out),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def _stream(stream):

@@ -1,0 +1,237 @@
+// Decode attention with learned sinks: one layer, up to 16 query tokens,
+// split over the positions a token sees (TandemLLM "21 Flint", 21.1 table rows
+// "attention", "sliding layers", "full layers"; How to Run Flint Locally,
+// "Sinks and the 513-token window").
+//
+//   k_attn_chunk    one workgroup per (chunk of 256 positions, KV head, token):
+//                   scores of the KV head's 8 query heads on the matrix cores
+//                   (keys bf16, the query split into three bf16 parts so that
+//                   every product is exact and the scores carry fp32
+//                   precision), the chunk's maximum, e^(s - m), their sum and
+//                   the weighted sum of the values -> one partial per head
+//   k_attn_combine  per (query head, token): the partials and the sink in
+//                   chunk order -> out
+// Each token's chunks are computed the same way whatever the other tokens
+// are, and every sum has a fixed order, so results are deterministic and
+// bitwise independent of the token count.
+#include "attn.h"
+
+namespace flint {
+
+namespace {
+
+constexpr int AQ = FLINT_ATT_Q_HEADS, AKV = FLINT_ATT_KV_HEADS, AD = FLINT_ATT_HEAD_DIM;
+constexpr int AG = AQ / AKV;   // query heads per KV head
+constexpr int ACH = 256;       // positions per chunk: 4 waves x 4 blocks of 16
+constexpr int APART = AD + 4;  // floats per partial: m, l, 2 unused, acc[AD]
+constexpr int ANT = 256;
+
+typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float at_f32x4 __attribute__((ext_vector_type(4)));
+
+// D = A B + C, 16 x 32 by 32 x 16: lane l holds row l % 16 of A and column
+// l % 16 of B for k = 8 (l / 16) .. + 7 (natural order on both); D register r
+// of lane l is row 4 (l / 16) + r, column l % 16.
+__device__ __forceinline__ at_f32x4 mfma16(uint4 a, uint4 b, at_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(at_bf16x8, a), __builtin_bit_cast(at_bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+
+}  // namespace
+
+// Per token: the first position it sees, how many, and its chunks.
+struct AttnTokens {
+  int first[FLINT_ATT_MAX_TOKENS];
+  int count[FLINT_ATT_MAX_TOKENS];
+  int nch[FLINT_ATT_MAX_TOKENS];
+};
+
+__global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q, const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v, int ring, AttnTokens T, int nch_max,
+                                                    float* __restrict__ ws) {
+  __shared__ float s_lds[ACH][AG];   // scores, then e^(s - m)
+  __shared__ float red[4][AG];
+  const int t = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  if (c >= T.nch[t]) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int p0 = T.first[t] + c * ACH;
+  const int cnt = min(ACH, T.first[t] + T.count[t] - p0);
+
+  // ---- scores.  B operand: column n = lane % 16 is query head 8 g + n / 2
+  // (n even: the query's high bf16 part, odd: the middle part); a second B
+  // carries the low part in the even columns.  q = hi + mid + lo exactly.
+  uint4 bq[4], bl[4];
+  {
+    const int n = lane & 15, h = AG * g + (n >> 1), odd = n & 1;
+    const float* qh = q + ((size_t)t * AQ + h) * AD;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int k0 = 32 * s + 8 * (lane >> 4);
+      const float4 x0 = *reinterpret_cast<const float4*>(qh + k0);
+      const float4 x1 = *reinterpret_cast<const float4*>(qh + k0 + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t w[8], wl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t hi = f32_to_bf16_rne(xs[i]);
+        const float r1 = xs[i] - bf16_bits_to_f32(hi);
+        const uint32_t mid = f32_to_bf16_rne(r1);
+        const uint32_t lo = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mid));
+        w[i] = odd ? mid : hi;
+        wl[i] = odd ? 0u : lo;
+      }
+      bq[s] = make_uint4(pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7]));
+      bl[s] = make_uint4(pack2(wl[0], wl[1]), pack2(wl[2], wl[3]), pack2(wl[4], wl[5]), pack2(wl[6], wl[7]));
+    }
+  }
+  // A operand: row = position 64 wave + 16 b + lane % 16 of the chunk; its
+  // key row is 256 contiguous bytes (rows past the chunk's end read an
+  // in-ring row and are masked below)
+  const float scale = 0.08838834764831845f;   // 1 / sqrt(128), exact to fp32 rounding
+  uint4 ka[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int j = 64 * wave + 16 * b + (lane & 15);
+    const uint4* kr = reinterpret_cast<const uint4*>(k + ((size_t)((p0 + j) % ring) * AKV + g) * AD);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ka[b][s] = kr[4 * s + (lane >> 4)];
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    at_f32x4 d = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      d = mfma16(ka[b][s], bq[s], d);
+      e = mfma16(ka[b][s], bl[s], e);
+    }
+    // lanes n, n ^ 1 hold the two parts of one head: (hi + mid) + lo
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float other = dpp_f32<DPP_XOR1>(d[r]);
+      const float sum = ((lane & 1) ? other + d[r] : d[r] + other) + e[r];   // hi + mid, then + lo
+      const int j = 64 * wave + 16 * b + 4 * (lane >> 4) + r;
+      if ((lane & 1) == 0) s_lds[j][(lane & 15) >> 1] = j < cnt ? sum * scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+
+  // ---- per head: chunk maximum, e^(s - m) and their sum (thread = position)
+  float sv[AG], m[AG];
+  {
+    const float4 s0 = *reinterpret_cast<const float4*>(&s_lds[tid][0]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&s_lds[tid][4]);
+    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+    sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+  }
+#pragma unroll
+  for (int h = 0; h < AG; ++h) {
+    float x = sv[h];
+    x = fmaxf(x, dpp_f32<DPP_XOR1>(x));
+    x = fmaxf(x, dpp_f32<DPP_XOR2>(x));
+    x = fmaxf(x, dpp_f32<DPP_HALF_MIRROR>(x));
+    x = fmaxf(x, dpp_f32<DPP_MIRROR>(x));
+    x = fmaxf(fmaxf(lane_bcast(x, 0), lane_bcast(x, 16)), fmaxf(lane_bcast(x, 32), lane_bcast(x, 48)));
+    if (lane == 0) red[wave][h] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < AG; ++h) m[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+  float ev[AG];
+#pragma unroll
+  for (int h = 0; h < AG; ++h) ev[h] = tid < cnt ? expf(sv[h] - m[h]) : 0.f;
+  *reinterpret_cast<float4*>(&s_lds[tid][0]) = make_float4(ev[0], ev[1], ev[2], ev[3]);
+  *reinterpret_cast<float4*>(&s_lds[tid][4]) = make_float4(ev[4], ev[5], ev[6], ev[7]);
+  __syncthreads();   // red is reused below; s_lds holds the weights
+  float lsum[AG];
+#pragma unroll
+  for (int h = 0; h < AG; ++h) {
+    const float x = wave_sum(ev[h]);   // fixed tree
+    if (lane == 0) red[wave][h] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < AG; ++h) lsum[h] = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
+
+  // ---- weighted values: thread = (dimension d, heads 4 hh .. 4 hh + 3),
+  // positions in order
+  const int d = tid & (AD - 1), hh = tid >> 7;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* vcol = v + (size_t)g * AD + d;
+  int j = 0;
+  for (; j + 8 <= cnt; j += 8) {
+    uint32_t vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vb[u] = vcol[(size_t)((p0 + j + u) % ring) * (AKV * AD)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&s_lds[j + u][4 * hh]);
+      const float vf = bf16_bits_to_f32(vb[u]);
+      acc[0] = fmaf(w4.x, vf, acc[0]);
+      acc[1] = fmaf(w4.y, vf, acc[1]);
+      acc[2] = fmaf(w4.z, vf, acc[2]);
+      acc[3] = fmaf(w4.w, vf, acc[3]);
+    }
+  }
+  for (; j < cnt; ++j) {
+    const float4 w4 = *reinterpret_cast<const float4*>(&s_lds[j][4 * hh]);
+    const float vf = bf16_bits_to_f32(vcol[(size_t)((p0 + j) % ring) * (AKV * AD)]);
+    acc[0] = fmaf(w4.x, vf, acc[0]);
+    acc[1] = fmaf(w4.y, vf, acc[1]);
+    acc[2] = fmaf(w4.z, vf, acc[2]);
+    acc[3] = fmaf(w4.w, vf, acc[3]);
+  }
+  // ---- partials
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * hh + i;
+    float* part = ws + (((size_t)t * AQ + AG * g + h) * nch_max + c) * APART;
+    part[4 + d] = acc[i];
+    if (d == 0) {
+      part[0] = m[h];
+      part[1] = lsum[h];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(AD) k_attn_combine(const float* __restrict__ sinks, AttnTokens T, int nch_max,
+                                                     const float* __restrict__ ws, float* __restrict__ out) {
+  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
+  const int nch = T.nch[t];
+  const float* part = ws + ((size_t)t * AQ + h) * nch_max * APART;
+  const float o = sinks[h];
+  float M = o;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, part[(size_t)c * APART]);
+  float L = expf(o - M), acc = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const float* pc = part + (size_t)c * APART;
+    const float f = expf(pc[0] - M);
+    L = fmaf(pc[1], f, L);
+    acc = fmaf(pc[4 + d], f, acc);
+  }
+  out[((size_t)t * AQ + h) * AD + d] = acc / L;
+}
+
+size_t attn_workspace_bytes(int n_tokens, int max_seen) {
+  const size_t nch = (size_t)(max_seen + ACH - 1) / ACH;
+  return (size_t)n_tokens * AQ * nch * APART * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int ring, const float* sinks,
+                              const int* first, const int* count, int n_tokens, float* out, float* ws,
+                              hipStream_t s) {
+  AttnTokens T = {};
+  int nch_max = 0;
+  for (int t = 0; t < n_tokens; ++t) {
+    T.first[t] = first[t];
+    T.count[t] = count[t];
+    T.nch[t] = (count[t] + ACH - 1) / ACH;
+    nch_max = max(nch_max, T.nch[t]);
+  }
+  hipLaunchKernelGGL(k_attn_chunk, dim3(nch_max, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max, ws);
+  hipLaunchKernelGGL(k_attn_combine, dim3(AQ, n_tokens), dim3(AD), 0, s, sinks, T, nch_max, ws, out);
+  return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,5 +1,6 @@
 // C ABI of the Flint MoE library: handle, argument validation, the
 // library-owned weight arena, workspaces, tracing and error reporting.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -7,6 +8,7 @@
 #include <string>
 #include <vector>
 
+#include "attn.h"
 #include "decode.h"
 #include "decode_persistent.h"
 #include "dense.h"
@@ -378,6 +380,46 @@ int flint_head_forward(flint_q4 head, int rows, const float* x, int n_tokens, fl
     return fail(FLINT_ERR_INVALID_ARG, "logits overlaps x");
   const hipError_t e = launch_head(head.codes, head.scales, rows, x, n_tokens, logits, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "head launch");
+  return FLINT_OK;
+}
+
+// ------------------------------------------------------------- decode attention
+size_t flint_attn_workspace_bytes(int n_tokens, int max_seen) {
+  if (n_tokens < 1 || n_tokens > FLINT_ATT_MAX_TOKENS || max_seen < 1) return 0;
+  return attn_workspace_bytes(n_tokens, max_seen);
+}
+
+int flint_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows, const float* sinks,
+                      const int32_t* pos, int n_tokens, int window, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !sinks || !pos || !out || !workspace)
+    return fail(FLINT_ERR_INVALID_ARG, "q, k, v, sinks, pos, out or workspace is NULL");
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(workspace))
+    return fail(FLINT_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
+  if (n_tokens < 1 || n_tokens > FLINT_ATT_MAX_TOKENS)
+    return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_ATT_MAX_TOKENS);
+  if (ring_rows < 1) return fail(FLINT_ERR_INVALID_ARG, "ring_rows = %d must be positive", ring_rows);
+  if (window < 0) return fail(FLINT_ERR_INVALID_ARG, "window = %d must not be negative", window);
+  int first[FLINT_ATT_MAX_TOKENS], count[FLINT_ATT_MAX_TOKENS], max_seen = 0;
+  for (int t = 0; t < n_tokens; ++t) {
+    if (pos[t] < 0) return fail(FLINT_ERR_INVALID_ARG, "pos[%d] = %d is negative", t, pos[t]);
+    first[t] = window ? std::max(0, pos[t] - window + 1) : 0;
+    count[t] = pos[t] - first[t] + 1;
+    if (count[t] > ring_rows)
+      return fail(FLINT_ERR_INVALID_ARG, "token %d sees %d positions, more than the %d cache rows", t, count[t],
+                  ring_rows);
+    max_seen = std::max(max_seen, count[t]);
+  }
+  const size_t need = attn_workspace_bytes(n_tokens, max_seen);
+  if (workspace_bytes < need)
+    return fail(FLINT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t qb = (size_t)n_tokens * FLINT_ATT_Q_HEADS * FLINT_ATT_HEAD_DIM * sizeof(float);
+  if (overlap(q, qb, out, qb)) return fail(FLINT_ERR_INVALID_ARG, "out overlaps q");
+  if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb))
+    return fail(FLINT_ERR_INVALID_ARG, "workspace overlaps q or out");
+  const hipError_t e = launch_attn_decode(q, k, v, ring_rows, sinks, first, count, n_tokens, out, (float*)workspace,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attention launch");
   return FLINT_OK;
 }
 

@@ -42,6 +42,38 @@ def test_constants_match_header():
     for name in ("FLINT_DENSE_MLP_SIZE", "FLINT_VOCAB", "FLINT_DENSE_MAX_TOKENS"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(F, name), name
+    text = open(os.path.join(INCLUDE, "flint_attn.h")).read()
+    for name in ("FLINT_ATT_Q_HEADS", "FLINT_ATT_KV_HEADS", "FLINT_ATT_HEAD_DIM", "FLINT_ATT_WINDOW", "FLINT_ATT_RING",
+                 "FLINT_ATT_MAX_TOKENS"):
+        m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(F, name), name
+
+
+def test_attention_rejects_bad_arguments_before_any_hip_call():
+    lib = F.lib()
+    A = 16   # any non-null, 16-byte aligned address: validation fails before it is used
+    ws = F.flint_attn_workspace_bytes(1, 513)
+    assert ws == 1 * 32 * 3 * 132 * 4
+    assert F.flint_attn_workspace_bytes(0, 513) == 0 and F.flint_attn_workspace_bytes(17, 513) == 0
+    assert F.flint_attn_workspace_bytes(1, 0) == 0
+    inval = F.FLINT_ERR_INVALID_ARG
+
+    def call(pos, n=None, window=513, ring=640, q=A, out=1 << 20, wsb=ws, ws_ptr=1 << 21):
+        n = len(pos) if n is None else n
+        p = (ctypes.c_int32 * max(1, len(pos)))(*pos)
+        return lib.flint_attn_decode(q, A, A, ring, A, p, n, window, out, ws_ptr, wsb, None)
+
+    assert call([10], n=0) == inval
+    assert call([10] * 17) == inval
+    assert call([-1]) == inval
+    assert call([10], ring=0) == inval
+    assert call([10], window=-1) == inval
+    assert call([700], window=0) == inval                  # 701 positions, 640 rows
+    assert call([5000], wsb=ws - 1) == inval               # window 513 fits the ring; workspace too small
+    assert call([10], q=A + 4) == inval                    # misaligned
+    assert call([10], out=A) == inval                      # out overlaps q
+    assert "overlaps" in F.flint_moe_last_error()
+    assert lib.flint_attn_decode(None, A, A, 640, A, (ctypes.c_int32 * 1)(3), 1, 513, A, A, ws, None) == inval
 
 
 def test_create_rejects_bad_arguments_before_any_hip_call():

@@ -1,0 +1,112 @@
+"""GPU parity of the decode attention with learned sinks against the oracle
+(TandemLLM "21 Flint", 21.1 table: 32 query heads, 4 KV heads of 128, a
+513-position window in a ring of 640 rows on window layers, every position on
+full layers; How to Run Flint Locally, "Sinks and the 513-token window").
+
+Seeded synthetic inputs: q, k, v ~ N(0, 1) (k and v stored as bf16), sink
+logits U(-9.0, 12.4) in bf16 (the checkpoint's range).
+
+Bound: scores are exact products summed in fp32 inside the matrix cores (the
+query in three bf16 parts), so their error is a few fp32 ulps of the sum of
+|q_i k_i| / sqrt(128) (about 1e-6 absolute).  The sums of e^(s - m) and of
+e^(s - m) v are fp32 in a fixed order over at most 256 positions per chunk and
+then over the chunks: relative error at most (256 + chunks) 2^-24, 4e-5 at
+100,000 positions, typically far less.  1e-4 relative L2 per token still fails
+a wrong head group, a dropped sink, a wrong scale or a window off by one
+position.
+"""
+import numpy as np
+import pytest
+import torch
+
+import flintgen as fg
+import int4_expert_ffn_amd as F
+from oracle import flint_oracle as O
+from parity_util import rel_l2
+
+pytestmark = pytest.mark.gpu
+REL_ATT = 1e-4
+
+
+def bf16_values(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).double().numpy()
+
+
+def run_attn(q, kb, vb, sinks, pos, window, ring):
+    n = len(pos)
+    max_seen = max((p - max(0, p - window + 1) + 1) if window else p + 1 for p in pos)
+    wsb = F.flint_attn_workspace_bytes(n, max_seen)
+    dev = torch.device("cuda")
+    qd = torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(dev)
+    kd = torch.from_numpy(np.ascontiguousarray(kb)).to(dev)
+    vd = torch.from_numpy(np.ascontiguousarray(vb)).to(dev)
+    sd = torch.from_numpy(np.ascontiguousarray(sinks, np.float32)).to(dev)
+    out = torch.empty((n, 32, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev)
+    F.flint_attn_decode(qd, kd, vd, ring, sd, pos, n, window, out, ws, wsb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(q, kb, vb, sinks, pos, window, out):
+    k, v = bf16_values(kb), bf16_values(vb)
+    errs = []
+    for t, p in enumerate(pos):
+        want = O.attention_decode(q[t].astype(np.float64), k, v, sinks, p, window)
+        err = rel_l2(out[t], want)
+        assert err <= REL_ATT, (t, p, err)
+        errs.append(err)
+    return errs
+
+
+def test_window_layer_positions_and_chunk_edges():
+    """Window layer, ring of 640 rows: the first positions (fewer than 513
+    visible), the chunk edges 256 / 257 / 512 / 513 visible, and positions far
+    past the ring's first wrap; all in one call of 10 tokens."""
+    ring, W = fg.ATT_RING, fg.ATT_WINDOW
+    kb, vb = fg.attn_cache(0, 1, ring)
+    sinks = fg.attn_sinks(0, 1)
+    pos = [0, 1, 100, 255, 256, 511, 512, 639, 1000, 70000]
+    q = fg.attn_queries(0, 1, len(pos))
+    out = run_attn(q, kb, vb, sinks, pos, W, ring)
+    errs = check(q, kb, vb, sinks, pos, W, out)
+    print(f"window layer: rel-L2 max {max(errs):.2e}")
+
+
+@pytest.mark.parametrize("n_pos", [4096, 100000])
+def test_full_layer_long_context(n_pos):
+    """Full layer: every position 0 .. pos, the ring as long as the context."""
+    kb, vb = fg.attn_cache(0, 2, n_pos)
+    sinks = fg.attn_sinks(0, 2)
+    pos = [n_pos - 1, n_pos // 2]
+    q = fg.attn_queries(0, 2, len(pos))
+    out = run_attn(q, kb, vb, sinks, pos, 0, n_pos)
+    errs = check(q, kb, vb, sinks, pos, 0, out)
+    print(f"full layer, {n_pos} positions: rel-L2 max {max(errs):.2e}")
+
+
+def test_tokens_independent_and_deterministic():
+    ring, W = fg.ATT_RING, fg.ATT_WINDOW
+    kb, vb = fg.attn_cache(0, 3, ring)
+    sinks = fg.attn_sinks(0, 3)
+    pos = [700 + 37 * i for i in range(16)]
+    q = fg.attn_queries(0, 3, 16)
+    all16 = run_attn(q, kb, vb, sinks, pos, W, ring)
+    again = run_attn(q, kb, vb, sinks, pos, W, ring)
+    assert np.array_equal(all16, again)
+    for t in (0, 5, 15):
+        alone = run_attn(q[t:t + 1], kb, vb, sinks, pos[t:t + 1], W, ring)
+        assert np.array_equal(alone[0], all16[t])
+
+
+def test_sink_extremes():
+    """Sinks at the checkpoint's extremes: at 12.4 the sink takes most of the
+    mass (the output shrinks toward 0), at -9 almost none."""
+    ring, W = fg.ATT_RING, fg.ATT_WINDOW
+    kb, vb = fg.attn_cache(0, 4, ring)
+    q = fg.attn_queries(0, 4, 2)
+    pos = [3, 900]
+    for value in (12.4, -9.0):
+        sinks = np.full(32, value, np.float32)
+        out = run_attn(q, kb, vb, sinks, pos, W, ring)
+        check(q, kb, vb, sinks, pos, W, out)
