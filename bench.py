@@ -381,6 +381,109 @@ def bench_head_dense(args):
     print(json.dumps(out), flush=True)
 
 
+ATT_BYTES_PER_POS = 2 * 4 * 128 * 2        # k and v rows of the 4 KV heads, bf16
+
+
+def bench_attn(args):
+    """Decode attention with learned sinks: a full layer at 100,000 positions
+    (the recipe's 100K decode context) for 1, 4 and 16 query tokens at
+    consecutive positions, and a window layer (513 positions in the 640-row
+    ring).  Two full-layer caches rotate so that the 256 MB last-level cache
+    cannot hold the 205 MB being read."""
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    dev = torch.device("cuda:0")
+    n_pos = 100000
+    caches = []
+    for i in range(2):
+        kb, vb = fg.attn_cache(0, 10 + i, n_pos)
+        caches.append((torch.from_numpy(kb).to(dev), torch.from_numpy(vb).to(dev)))
+    wk, wv = (torch.from_numpy(x).to(dev) for x in fg.attn_cache(0, 20, fg.ATT_RING))
+    sinks = torch.from_numpy(fg.attn_sinks(0, 10)).to(dev)
+    q = torch.from_numpy(fg.attn_queries(0, 10, 16)).to(dev)
+    out = torch.empty((16, 32, 128), dtype=torch.float32, device=dev)
+    wsb = F.flint_attn_workspace_bytes(16, n_pos)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        for i in range(args.warmup):
+            call(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            call(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        return float(np.median(d)), float(np.mean(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+    def full(n):
+        pos = [n_pos - n + i for i in range(n)]
+        def call(i):
+            k, v = caches[i % 2]
+            F.flint_attn_decode(q, k, v, n_pos, sinks, pos, n, 0, out, ws, wsb, stream)
+        return call
+
+    def window(n):
+        pos = [5000 + i for i in range(n)]
+        return lambda i: F.flint_attn_decode(q, wk, wv, fg.ATT_RING, sinks, pos, n, fg.ATT_WINDOW, out, ws, wsb, stream)
+
+    res_full = {n: timed(full(n)) for n in (1, 4, 16)}
+    res_win = {n: timed(window(n)) for n in (1, 16)}
+    med, mean = res_full[1][0], res_full[1][1]
+    algo = n_pos * ATT_BYTES_PER_POS + 2 * 32 * 128 * 4 + 32 * 4
+    achieved = algo / mean / 1e9
+    outj = {
+        "metric": "decode attention with sinks, achieved HBM GB/s (full layer, 100,000 positions, batch 1)",
+        "value": round(algo / med / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(med * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 KV x fp32 q (MFMA bf16, q in three parts) -> fp32",
+        "data": "synthetic (seeded N(0,1) q, k, v; sink logits U(-9, 12.4))",
+        "config": {"workload": "one full attention layer at 100,000 positions and one window layer (513 of a "
+                               "640-row ring), 32 query / 4 KV heads of 128", "positions": n_pos,
+                   "algorithmic_bytes_batch1": algo},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "k_attn_chunk + k_attn_combine (one call, hip events; mean duration)"},
+        "full_layer_us": {str(n): [round(v * 1e6, 2) for v in (r[0], r[2], r[3])] for n, r in res_full.items()},
+        "window_layer_us": {str(n): [round(v * 1e6, 2) for v in (r[0], r[2], r[3])] for n, r in res_win.items()},
+        "timing_note": "median, p10, p90 of hip-event call durations; n tokens at consecutive positions share the "
+                       "cache, which each call reads once per token",
+    }
+    if not args.no_cpu_baseline:
+        outj["cpu_baseline"] = cpu_baseline_attn(args.cpu_seconds)
+    print(json.dumps(outj), flush=True)
+
+
+def cpu_baseline_attn(seconds_budget=20.0):
+    """The CPU oracle on a bounded sample: one token of a full layer at 100,000
+    positions (all 32 query heads, one oracle call, repeated while the budget
+    allows); scaled to GB/s of cache read."""
+    import flintgen as fg
+    import torch
+    from oracle import flint_oracle as O
+    n_pos = 100000
+    kb, vb = fg.attn_cache(0, 10, n_pos)
+    k = torch.from_numpy(kb).view(torch.bfloat16).double().numpy()
+    v = torch.from_numpy(vb).view(torch.bfloat16).double().numpy()
+    q = fg.attn_queries(0, 10, 1)[0].astype(np.float64)
+    sinks = fg.attn_sinks(0, 10)
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        O.attention_decode(q, k, v, sinks, n_pos - 1, 0)
+        calls += 1
+        if time.perf_counter() - t0 > min(seconds_budget, 5.0) or calls >= 20:
+            break
+    dt = (time.perf_counter() - t0) / calls
+    return {"value": round(n_pos * ATT_BYTES_PER_POS / dt / 1e9, 4), "unit": "GB/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"one token, 32 query heads, 100,000 positions; {calls} oracle calls, "
+                                        f"{dt:.2f} s each"}
+
+
 def _oracle_threads():
     try:
         import threadpoolctl
@@ -488,6 +591,8 @@ def main():
     ap.add_argument("--cost-table", action="store_true",
                     help="time one 47-layer call for n = 1..16 tokens (verify-block cost table)")
     ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
+    ap.add_argument("--attn", action="store_true",
+                    help="time the decode attention with sinks instead (full layer at 100,000 positions, window layer)")
     ap.add_argument("--interm-div", type=int, default=0,
                     help="time the fp16-intermediate form instead: the same stack with routed up projections "
                          "divided by this power of two (128 in the published packs)")
@@ -503,6 +608,9 @@ def main():
         return
     if args.head_dense:
         bench_head_dense(args)
+        return
+    if args.attn:
+        bench_attn(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

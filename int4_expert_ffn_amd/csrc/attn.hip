@@ -9,8 +9,9 @@
 //                   every product is exact and the scores carry fp32
 //                   precision), the chunk's maximum, e^(s - m), their sum and
 //                   the weighted sum of the values -> one partial per head
-//   k_attn_combine  per (query head, token): the partials and the sink in
-//                   chunk order -> out
+//   k_attn_combine  per (query head, token): the partials and the sink in a
+//                   fixed order (8 interleaved subsets of the chunks, each in
+//                   chunk order, then the subsets in order) -> out
 // Each token's chunks are computed the same way whatever the other tokens
 // are, and every sum has a fixed order, so results are deterministic and
 // bitwise independent of the token count.
@@ -53,6 +54,7 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
                                                     float* __restrict__ ws) {
   __shared__ float s_lds[ACH][AG];   // scores, then e^(s - m)
   __shared__ float red[4][AG];
+  __shared__ __align__(16) uint16_t v_lds[ACH][AD];   // the chunk's value rows of this KV head (64 KB)
   const int t = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (c >= T.nch[t]) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -98,6 +100,23 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
     for (int s = 0; s < 4; ++s) ka[b][s] = kr[4 * s + (lane >> 4)];
   }
+  // the chunk's value rows: 8 threads per 256-byte row, 32 bytes each (rows
+  // past the chunk's end repeat its first row), all requested now and written
+  // to LDS after the scores
+  uint4 vst[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 32 * i + (tid >> 3), piece = tid & 7;   // rows 32 i .. 32 i + 31
+    const int jj = j < cnt ? j : 0;
+    vst[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece];
+  }
+  uint4 vst2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 32 * i + (tid >> 3), piece = tid & 7;
+    const int jj = j < cnt ? j : 0;
+    vst2[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece + 1];
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     at_f32x4 d = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
@@ -114,6 +133,12 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
       const int j = 64 * wave + 16 * b + 4 * (lane >> 4) + r;
       if ((lane & 1) == 0) s_lds[j][(lane & 15) >> 1] = j < cnt ? sum * scale : -INFINITY;
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int j = 32 * i + (tid >> 3), piece = tid & 7;
+    reinterpret_cast<uint4*>(&v_lds[j][0])[2 * piece] = vst[i];
+    reinterpret_cast<uint4*>(&v_lds[j][0])[2 * piece + 1] = vst2[i];
   }
   __syncthreads();
 
@@ -158,25 +183,9 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   // positions in order
   const int d = tid & (AD - 1), hh = tid >> 7;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* vcol = v + (size_t)g * AD + d;
-  int j = 0;
-  for (; j + 8 <= cnt; j += 8) {
-    uint32_t vb[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) vb[u] = vcol[(size_t)((p0 + j + u) % ring) * (AKV * AD)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float4 w4 = *reinterpret_cast<const float4*>(&s_lds[j + u][4 * hh]);
-      const float vf = bf16_bits_to_f32(vb[u]);
-      acc[0] = fmaf(w4.x, vf, acc[0]);
-      acc[1] = fmaf(w4.y, vf, acc[1]);
-      acc[2] = fmaf(w4.z, vf, acc[2]);
-      acc[3] = fmaf(w4.w, vf, acc[3]);
-    }
-  }
-  for (; j < cnt; ++j) {
+  for (int j = 0; j < cnt; ++j) {
     const float4 w4 = *reinterpret_cast<const float4*>(&s_lds[j][4 * hh]);
-    const float vf = bf16_bits_to_f32(vcol[(size_t)((p0 + j) % ring) * (AKV * AD)]);
+    const float vf = bf16_bits_to_f32(v_lds[j][d]);
     acc[0] = fmaf(w4.x, vf, acc[0]);
     acc[1] = fmaf(w4.y, vf, acc[1]);
     acc[2] = fmaf(w4.z, vf, acc[2]);
@@ -195,22 +204,70 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   }
 }
 
-__global__ void __launch_bounds__(AD) k_attn_combine(const float* __restrict__ sinks, AttnTokens T, int nch_max,
-                                                     const float* __restrict__ ws, float* __restrict__ out) {
-  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
+// One workgroup per (query head, token): 8 waves' worth of threads = 128
+// dimensions x 8 chunk subsets.  M = max(o, m_c) over the chunks (exact);
+// f_c = e^(m_c - M); L = e^(o - M) + sum_c l_c f_c and O = sum_c acc_c f_c,
+// each subset summing its chunks c = sub, sub + 8, ... in order, then the 8
+// subsets in order.
+constexpr int ACS = 8;   // chunk subsets
+__global__ void __launch_bounds__(AD * ACS) k_attn_combine(const float* __restrict__ sinks, AttnTokens T,
+                                                           int nch_max, const float* __restrict__ ws,
+                                                           float* __restrict__ out) {
+  __shared__ float mred[AD * ACS / 64];
+  __shared__ float lsub[ACS], osub[ACS][AD];
+  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, d = tid & (AD - 1), sub = tid >> 7;
+  const int lane = tid & 63, wave = tid >> 6;
   const int nch = T.nch[t];
   const float* part = ws + ((size_t)t * AQ + h) * nch_max * APART;
   const float o = sinks[h];
-  float M = o;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, part[(size_t)c * APART]);
-  float L = expf(o - M), acc = 0.f;
-  for (int c = 0; c < nch; ++c) {
+  float mx = o;
+  for (int c = tid; c < nch; c += AD * ACS) mx = fmaxf(mx, part[(size_t)c * APART]);
+  mx = fmaxf(mx, dpp_f32<DPP_XOR1>(mx));
+  mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
+  mx = fmaxf(mx, dpp_f32<DPP_HALF_MIRROR>(mx));
+  mx = fmaxf(mx, dpp_f32<DPP_MIRROR>(mx));
+  mx = fmaxf(fmaxf(lane_bcast(mx, 0), lane_bcast(mx, 16)), fmaxf(lane_bcast(mx, 32), lane_bcast(mx, 48)));
+  if (lane == 0) mred[wave] = mx;
+  __syncthreads();
+  float M = mred[0];
+#pragma unroll
+  for (int i = 1; i < AD * ACS / 64; ++i) M = fmaxf(M, mred[i]);
+  float L = 0.f, acc = 0.f;
+  int c = sub;
+  for (; c + 3 * ACS < nch; c += 4 * ACS) {   // four chunks of this subset in flight
+    float mc[4], lc[4], ac[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* pc = part + (size_t)(c + u * ACS) * APART;
+      mc[u] = pc[0];
+      lc[u] = pc[1];
+      ac[u] = pc[4 + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float f = expf(mc[u] - M);
+      L = fmaf(lc[u], f, L);
+      acc = fmaf(ac[u], f, acc);
+    }
+  }
+  for (; c < nch; c += ACS) {
     const float* pc = part + (size_t)c * APART;
     const float f = expf(pc[0] - M);
     L = fmaf(pc[1], f, L);
     acc = fmaf(pc[4 + d], f, acc);
   }
-  out[((size_t)t * AQ + h) * AD + d] = acc / L;
+  osub[sub][d] = acc;
+  if (d == 0) lsub[sub] = L;
+  __syncthreads();
+  if (sub == 0) {
+    float Lt = expf(o - M), At = 0.f;
+#pragma unroll
+    for (int i = 0; i < ACS; ++i) {
+      Lt += lsub[i];
+      At += osub[i][d];
+    }
+    out[((size_t)t * AQ + h) * AD + d] = At / Lt;
+  }
 }
 
 size_t attn_workspace_bytes(int n_tokens, int max_seen) {
@@ -230,7 +287,7 @@ hipError_t launch_attn_decode(const float* q, const uint16_t* k, const uint16_t*
     nch_max = max(nch_max, T.nch[t]);
   }
   hipLaunchKernelGGL(k_attn_chunk, dim3(nch_max, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max, ws);
-  hipLaunchKernelGGL(k_attn_combine, dim3(AQ, n_tokens), dim3(AD), 0, s, sinks, T, nch_max, ws, out);
+  hipLaunchKernelGGL(k_attn_combine, dim3(AQ, n_tokens), dim3(AD * ACS), 0, s, sinks, T, nch_max, ws, out);
   return hipGetLastError();
 }
 
