@@ -431,8 +431,8 @@ def bench_attn(args):
         pos = [5000 + i for i in range(n)]
         return lambda i: F.flint_attn_decode(q, wk, wv, fg.ATT_RING, sinks, pos, n, fg.ATT_WINDOW, out, ws, wsb, stream)
 
-    res_full = {n: timed(full(n)) for n in (1, 4, 16)}
-    res_win = {n: timed(window(n)) for n in (1, 16)}
+    res_full = {n: timed(full(n)) for n in ((1,) if args.attn_batch1 else (1, 4, 16))}
+    res_win = {} if args.attn_batch1 else {n: timed(window(n)) for n in (1, 16)}
     med, mean = res_full[1][0], res_full[1][1]
     algo = n_pos * ATT_BYTES_PER_POS + 2 * 32 * 128 * 4 + 32 * 4
     achieved = algo / mean / 1e9
@@ -593,6 +593,8 @@ def main():
     ap.add_argument("--cost-table-out", default=None, help="write the cost table (CSV with a header) to this file")
     ap.add_argument("--attn", action="store_true",
                     help="time the decode attention with sinks instead (full layer at 100,000 positions, window layer)")
+    ap.add_argument("--attn-batch1", action="store_true",
+                    help="with --attn: only the batch-1 full layer (for a kernel trace of that one shape)")
     ap.add_argument("--interm-div", type=int, default=0,
                     help="time the fp16-intermediate form instead: the same stack with routed up projections "
                          "divided by this power of two (128 in the published packs)")
