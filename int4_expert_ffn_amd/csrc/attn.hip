@@ -8,7 +8,8 @@
 //                   (keys bf16, the query split into three bf16 parts so that
 //                   every product is exact and the scores carry fp32
 //                   precision), the chunk's maximum, e^(s - m), their sum and
-//                   the weighted sum of the values -> one partial per head
+//                   the weighted sum of the values, also on the matrix cores
+//                   (the weights as two bf16 parts) -> one partial per head
 //   k_attn_combine  per (query head, token): the partials and the sink in a
 //                   fixed order (8 interleaved subsets of the chunks, each in
 //                   chunk order, then the subsets in order) -> out
@@ -26,6 +27,7 @@ constexpr int AG = AQ / AKV;   // query heads per KV head
 constexpr int ACH = 256;       // positions per chunk: 4 waves x 4 blocks of 16
 constexpr int APART = AD + 4;  // floats per partial: m, l, 2 unused, acc[AD]
 constexpr int ANT = 256;
+constexpr int AVP = AD + 4;    // padded value row (u16)
 
 typedef __bf16 at_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float at_f32x4 __attribute__((ext_vector_type(4)));
@@ -52,9 +54,16 @@ struct AttnTokens {
 __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, int ring, AttnTokens T, int nch_max,
                                                     float* __restrict__ ws) {
-  __shared__ float s_lds[ACH][AG];   // scores, then e^(s - m)
+  // scores [position][head]; once they are in registers the same memory holds
+  // e^(s - m) as two bf16 parts [2 h + part][position]
+  __shared__ __align__(16) float sp_lds[ACH * AG];
+  float (*const s_lds)[AG] = reinterpret_cast<float (*)[AG]>(sp_lds);
+  uint16_t (*const p16)[ACH] = reinterpret_cast<uint16_t (*)[ACH]>(sp_lds);
+  static_assert(2 * AG * ACH * 2 == ACH * AG * 4, "weights reuse the score memory");
   __shared__ float red[4][AG];
-  __shared__ __align__(16) uint16_t v_lds[ACH][AD];   // the chunk's value rows of this KV head (64 KB)
+  // the chunk's value rows of this KV head, rows padded to 264 bytes so that
+  // the matrix-core operand reads (16 dimensions x rows 8 apart) hit distinct banks
+  __shared__ __align__(16) uint16_t v_lds[ACH][AVP];
   const int t = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   if (c >= T.nch[t]) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -137,8 +146,11 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int j = 32 * i + (tid >> 3), piece = tid & 7;
-    reinterpret_cast<uint4*>(&v_lds[j][0])[2 * piece] = vst[i];
-    reinterpret_cast<uint4*>(&v_lds[j][0])[2 * piece + 1] = vst2[i];
+    uint2* row = reinterpret_cast<uint2*>(&v_lds[j][0]) + 4 * piece;
+    row[0] = make_uint2(vst[i].x, vst[i].y);
+    row[1] = make_uint2(vst[i].z, vst[i].w);
+    row[2] = make_uint2(vst2[i].x, vst2[i].y);
+    row[3] = make_uint2(vst2[i].z, vst2[i].w);
   }
   __syncthreads();
 
@@ -165,10 +177,13 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   for (int h = 0; h < AG; ++h) m[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
   float ev[AG];
 #pragma unroll
-  for (int h = 0; h < AG; ++h) ev[h] = tid < cnt ? expf(sv[h] - m[h]) : 0.f;
-  *reinterpret_cast<float4*>(&s_lds[tid][0]) = make_float4(ev[0], ev[1], ev[2], ev[3]);
-  *reinterpret_cast<float4*>(&s_lds[tid][4]) = make_float4(ev[4], ev[5], ev[6], ev[7]);
-  __syncthreads();   // red is reused below; s_lds holds the weights
+  for (int h = 0; h < AG; ++h) {
+    ev[h] = tid < cnt ? expf(sv[h] - m[h]) : 0.f;
+    const uint32_t hi = f32_to_bf16_rne(ev[h]);
+    p16[2 * h][tid] = (uint16_t)hi;
+    p16[2 * h + 1][tid] = (uint16_t)f32_to_bf16_rne(ev[h] - bf16_bits_to_f32(hi));
+  }
+  __syncthreads();   // red is reused below; p16 holds the weights (the scores were read before the last barrier)
   float lsum[AG];
 #pragma unroll
   for (int h = 0; h < AG; ++h) {
@@ -179,29 +194,41 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
 #pragma unroll
   for (int h = 0; h < AG; ++h) lsum[h] = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
 
-  // ---- weighted values: thread = (dimension d, heads 4 hh .. 4 hh + 3),
-  // positions in order
-  const int d = tid & (AD - 1), hh = tid >> 7;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < cnt; ++j) {
-    const float4 w4 = *reinterpret_cast<const float4*>(&s_lds[j][4 * hh]);
-    const float vf = bf16_bits_to_f32(v_lds[j][d]);
-    acc[0] = fmaf(w4.x, vf, acc[0]);
-    acc[1] = fmaf(w4.y, vf, acc[1]);
-    acc[2] = fmaf(w4.z, vf, acc[2]);
-    acc[3] = fmaf(w4.w, vf, acc[3]);
-  }
-  // ---- partials
+  // ---- weighted values on the matrix cores: O^T[d][2 h + part] =
+  // sum_p V[p][d] P16[2 h + part][p] (A: 16 dimensions x 32 positions, the
+  // value column gathered from LDS; B: 32 positions x 16 weight rows), all
+  // 256 positions in 8 steps; O[h][d] = part 0 + part 1.  Wave w takes the
+  // dimensions 32 w .. 32 w + 31 (two blocks of 16).
+  at_f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * hh + i;
-    float* part = ws + (((size_t)t * AQ + AG * g + h) * nch_max + c) * APART;
-    part[4 + d] = acc[i];
-    if (d == 0) {
+  for (int st = 0; st < ACH / 32; ++st) {
+    const int kb = 32 * st + 8 * (lane >> 4);
+    const uint4 bp = *reinterpret_cast<const uint4*>(&p16[lane & 15][kb]);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int dd = 32 * wave + 16 * db + (lane & 15);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)v_lds[kb + 2 * i][dd] | ((uint32_t)v_lds[kb + 2 * i + 1][dd] << 16);
+      o[db] = mfma16(make_uint4(w[0], w[1], w[2], w[3]), bp, o[db]);
+    }
+  }
+  // ---- partials: lanes with an even column hold head (lane % 16) / 2
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float other = dpp_f32<DPP_XOR1>(o[db][r]);
+      const int h = (lane & 15) >> 1, dd = 32 * wave + 16 * db + 4 * (lane >> 4) + r;
+      if ((lane & 1) == 0) ws[(((size_t)t * AQ + AG * g + h) * nch_max + c) * APART + 4 + dd] = o[db][r] + other;
+    }
+#pragma unroll
+  for (int h = 0; h < AG; ++h)
+    if (tid == h) {
+      float* part = ws + (((size_t)t * AQ + AG * g + h) * nch_max + c) * APART;
       part[0] = m[h];
       part[1] = lsum[h];
     }
-  }
 }
 
 // One workgroup per (query head, token): 8 waves' worth of threads = 128
