@@ -10,9 +10,10 @@
 //                   precision), the chunk's maximum, e^(s - m), their sum and
 //                   the weighted sum of the values, also on the matrix cores
 //                   (the weights as two bf16 parts) -> one partial per head
-//   k_attn_combine  per (query head, token): the partials and the sink in a
-//                   fixed order (8 interleaved subsets of the chunks, each in
-//                   chunk order, then the subsets in order) -> out
+//   k_attn_combine  per (query head, 32 dimensions, token): the partials and
+//                   the sink in a fixed order (8 interleaved subsets of the
+//                   chunks, each in chunk order, then the subsets in order)
+//                   -> out
 // Each token's chunks are computed the same way whatever the other tokens
 // are, and every sum has a fixed order, so results are deterministic and
 // bitwise independent of the token count.
@@ -231,24 +232,26 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     }
 }
 
-// One workgroup per (query head, token): 8 waves' worth of threads = 128
-// dimensions x 8 chunk subsets.  M = max(o, m_c) over the chunks (exact);
+// One workgroup per (query head, 32 dimensions, token): 32 dimensions x 8
+// chunk subsets.  M = max(o, m_c) over the chunks (exact);
 // f_c = e^(m_c - M); L = e^(o - M) + sum_c l_c f_c and O = sum_c acc_c f_c,
 // each subset summing its chunks c = sub, sub + 8, ... in order, then the 8
 // subsets in order.
-constexpr int ACS = 8;   // chunk subsets
-__global__ void __launch_bounds__(AD * ACS) k_attn_combine(const float* __restrict__ sinks, AttnTokens T,
-                                                           int nch_max, const float* __restrict__ ws,
-                                                           float* __restrict__ out) {
-  __shared__ float mred[AD * ACS / 64];
-  __shared__ float lsub[ACS], osub[ACS][AD];
-  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, d = tid & (AD - 1), sub = tid >> 7;
+constexpr int ACS = 8;          // chunk subsets
+constexpr int ACD = AD / 4;     // dimensions per workgroup
+__global__ void __launch_bounds__(ACD * ACS) k_attn_combine(const float* __restrict__ sinks, AttnTokens T,
+                                                            int nch_max, const float* __restrict__ ws,
+                                                            float* __restrict__ out) {
+  __shared__ float mred[ACD * ACS / 64];
+  __shared__ float lsub[ACS], osub[ACS][ACD];
+  const int h = blockIdx.x, dq = blockIdx.y, t = blockIdx.z, tid = threadIdx.x;
+  const int dl = tid % ACD, sub = tid / ACD, d = ACD * dq + dl;
   const int lane = tid & 63, wave = tid >> 6;
   const int nch = T.nch[t];
   const float* part = ws + ((size_t)t * AQ + h) * nch_max * APART;
   const float o = sinks[h];
   float mx = o;
-  for (int c = tid; c < nch; c += AD * ACS) mx = fmaxf(mx, part[(size_t)c * APART]);
+  for (int c = tid; c < nch; c += ACD * ACS) mx = fmaxf(mx, part[(size_t)c * APART]);
   mx = fmaxf(mx, dpp_f32<DPP_XOR1>(mx));
   mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
   mx = fmaxf(mx, dpp_f32<DPP_HALF_MIRROR>(mx));
@@ -258,20 +261,21 @@ __global__ void __launch_bounds__(AD * ACS) k_attn_combine(const float* __restri
   __syncthreads();
   float M = mred[0];
 #pragma unroll
-  for (int i = 1; i < AD * ACS / 64; ++i) M = fmaxf(M, mred[i]);
+  for (int i = 1; i < ACD * ACS / 64; ++i) M = fmaxf(M, mred[i]);
   float L = 0.f, acc = 0.f;
   int c = sub;
-  for (; c + 3 * ACS < nch; c += 4 * ACS) {   // four chunks of this subset in flight
-    float mc[4], lc[4], ac[4];
+  constexpr int AU = 8;   // chunks of this subset in flight
+  for (; c + (AU - 1) * ACS < nch; c += AU * ACS) {
+    float mc[AU], lc[AU], ac[AU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < AU; ++u) {
       const float* pc = part + (size_t)(c + u * ACS) * APART;
       mc[u] = pc[0];
       lc[u] = pc[1];
       ac[u] = pc[4 + d];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < AU; ++u) {
       const float f = expf(mc[u] - M);
       L = fmaf(lc[u], f, L);
       acc = fmaf(ac[u], f, acc);
@@ -283,15 +287,15 @@ __global__ void __launch_bounds__(AD * ACS) k_attn_combine(const float* __restri
     L = fmaf(pc[1], f, L);
     acc = fmaf(pc[4 + d], f, acc);
   }
-  osub[sub][d] = acc;
-  if (d == 0) lsub[sub] = L;
+  osub[sub][dl] = acc;
+  if (dl == 0) lsub[sub] = L;
   __syncthreads();
   if (sub == 0) {
     float Lt = expf(o - M), At = 0.f;
 #pragma unroll
     for (int i = 0; i < ACS; ++i) {
       Lt += lsub[i];
-      At += osub[i][d];
+      At += osub[i][dl];
     }
     out[((size_t)t * AQ + h) * AD + d] = At / Lt;
   }
@@ -314,7 +318,7 @@ hipError_t launch_attn_decode(const float* q, const uint16_t* k, const uint16_t*
     nch_max = max(nch_max, T.nch[t]);
   }
   hipLaunchKernelGGL(k_attn_chunk, dim3(nch_max, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max, ws);
-  hipLaunchKernelGGL(k_attn_combine, dim3(AQ, n_tokens), dim3(AD * ACS), 0, s, sinks, T, nch_max, ws, out);
+  hipLaunchKernelGGL(k_attn_combine, dim3(AQ, AD / ACD, n_tokens), dim3(ACD * ACS), 0, s, sinks, T, nch_max, ws, out);
   return hipGetLastError();
 }
 
