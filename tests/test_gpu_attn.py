@@ -110,3 +110,20 @@ def test_sink_extremes():
         sinks = np.full(32, value, np.float32)
         out = run_attn(q, kb, vb, sinks, pos, W, ring)
         check(q, kb, vb, sinks, pos, W, out)
+
+
+@pytest.mark.parametrize("n_pos", [20000, 100000])
+def test_verify_block_tokens_independent(n_pos):
+    """A verify block: tokens at neighbouring positions of a full layer, plus
+    one far earlier.  Each token's result must equal the token run alone,
+    bitwise, and the oracle."""
+    kb, vb = fg.attn_cache(0, 5, n_pos)
+    sinks = fg.attn_sinks(0, 5)
+    pos = [n_pos - 16 + i for i in range(15)] + [300]
+    q = fg.attn_queries(0, 5, len(pos))
+    out = run_attn(q, kb, vb, sinks, pos, 0, n_pos)
+    for t in (0, 7, 14, 15):
+        alone = run_attn(q[t:t + 1], kb, vb, sinks, pos[t:t + 1], 0, n_pos)
+        assert np.array_equal(alone[0], out[t]), t
+    errs = check(q[[0, 14, 15]], kb, vb, sinks, [pos[0], pos[14], pos[15]], 0, out[[0, 14, 15]])
+    print(f"verify block, {n_pos} positions: rel-L2 max {max(errs):.2e}")
