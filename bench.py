@@ -484,6 +484,26 @@ def cpu_baseline_attn(seconds_budget=20.0):
                                         f"{dt:.2f} s each"}
 
 
+def measure_copy_gbps(torch, dev, n_bytes=1 << 30, reps=10):
+    """Bandwidth of a plain device-to-device copy of 1 GiB (read + write bytes
+    per second, hip events): the attainable HBM rate the roofline fraction can
+    also be read against."""
+    a = torch.empty(n_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n_bytes / sec / 1e9
+
+
 def _oracle_threads():
     try:
         import threadpoolctl
@@ -692,6 +712,9 @@ def main():
                      "launch_us_p90": round(float(np.percentile(durs, 90)) * 1e6, 2)},
         "setup_s": round(setup_s, 1),
     }
+    copy_gbps = measure_copy_gbps(torch, dev)
+    res["roofline"]["copy_gbps"] = round(copy_gbps, 1)
+    res["roofline"]["frac_of_copy"] = round(achieved / copy_gbps, 4)
     if args.interm_div:
         res["config"]["interm_div"] = args.interm_div
         res["roofline"]["traffic"] = None   # the counters were taken on the fp32 form
