@@ -1,0 +1,39 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU guard, the
+algorithmic byte counts it prices the roofline with, and the traffic summary
+lookup keyed to the profiled kernel's own sources."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_algorithmic_bytes_match_the_block_shapes():
+    # per layer: bf16 router + fp32 bias, six routed experts and the shared one
+    # (int4 codes + one bf16 scale per 128 inputs), as the scope table counts them
+    assert bench.EXPERT_BYTES == 3 * (512 * 2048 // 2 + 512 * 2048 // 128 * 2) == 1622016
+    assert bench.SHARED_BYTES == 3 * (1024 * 2048 // 2 + 1024 * 2048 // 128 * 2) == 3244032
+    assert bench.LAYER_BYTES == 14025728
+    assert bench.TOKEN_BYTES == 47 * 14025728 == 659209216
+    assert bench.HEAD_BYTES == 150144 * (1024 + 32)
+    assert bench.ATT_BYTES_PER_POS == 2048
+
+
+def test_traffic_summary_only_counts_for_its_own_sources(tmp_path):
+    p = tmp_path / "traffic.txt"
+    p.write_text(f"kernel_source_hash: {bench.kernel_source_hash('decode')}\nhbm_bytes_per_launch: 1234\n")
+    assert bench.traffic_from_profiles(str(p), "decode") == 1234
+    assert bench.traffic_from_profiles(str(p), "head") is None          # another kernel's sources
+    p.write_text("kernel_source_hash: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
+    assert bench.traffic_from_profiles(str(p), "decode") is None
+    assert bench.traffic_from_profiles(str(tmp_path / "missing.txt")) is None
