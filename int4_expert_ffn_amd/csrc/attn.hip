@@ -3,7 +3,8 @@
 // "attention", "sliding layers", "full layers"; How to Run Flint Locally,
 // "Sinks and the 513-token window").
 //
-//   k_attn_chunk    one workgroup per (chunk of 256 positions, KV head, token):
+//   k_attn_chunk    one workgroup per (chunk of 256 positions, or of 64 for a
+//                   token that sees at most 768, KV head, token):
 //                   scores of the KV head's 8 query heads on the matrix cores
 //                   (keys bf16, the query split into three bf16 parts so that
 //                   every product is exact and the scores carry fp32
@@ -45,31 +46,40 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo 
 
 }  // namespace
 
-// Per token: the first position it sees, how many, and its chunks.
+// Per token: the first position it sees, how many, its chunks, and the chunk
+// size (ACH, or ACH_S for a token that sees at most ACH_SMAX positions: more
+// workgroups for short ranges such as the 513-position window).
 struct AttnTokens {
   int first[FLINT_ATT_MAX_TOKENS];
   int count[FLINT_ATT_MAX_TOKENS];
   int nch[FLINT_ATT_MAX_TOKENS];
+  int chunk[FLINT_ATT_MAX_TOKENS];
 };
+constexpr int ACH_S = 64, ACH_SMAX = 768;
 
+// CH positions per workgroup (a multiple of 64): wave w scores positions
+// 64 w' + 16 b of the chunk for its CH / 64 blocks; tokens whose chunk size is
+// not CH are left to the other instance.
+template <int CH>
 __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, int ring, AttnTokens T, int nch_max,
                                                     float* __restrict__ ws) {
+  constexpr int BW = CH / 64;   // blocks of 16 positions per wave (CH / 4 positions per wave)
   // scores [position][head]; once they are in registers the same memory holds
   // e^(s - m) as two bf16 parts [2 h + part][position]
-  __shared__ __align__(16) float sp_lds[ACH * AG];
+  __shared__ __align__(16) float sp_lds[CH * AG];
   float (*const s_lds)[AG] = reinterpret_cast<float (*)[AG]>(sp_lds);
-  uint16_t (*const p16)[ACH] = reinterpret_cast<uint16_t (*)[ACH]>(sp_lds);
-  static_assert(2 * AG * ACH * 2 == ACH * AG * 4, "weights reuse the score memory");
+  uint16_t (*const p16)[CH] = reinterpret_cast<uint16_t (*)[CH]>(sp_lds);
+  static_assert(2 * AG * CH * 2 == CH * AG * 4, "weights reuse the score memory");
   __shared__ float red[4][AG];
   // the chunk's value rows of this KV head, rows padded to 264 bytes so that
   // the matrix-core operand reads (16 dimensions x rows 8 apart) hit distinct banks
-  __shared__ __align__(16) uint16_t v_lds[ACH][AVP];
+  __shared__ __align__(16) uint16_t v_lds[CH][AVP];
   const int t = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
-  if (c >= T.nch[t]) return;
+  if (T.chunk[t] != CH || c >= T.nch[t]) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int p0 = T.first[t] + c * ACH;
-  const int cnt = min(ACH, T.first[t] + T.count[t] - p0);
+  const int p0 = T.first[t] + c * CH;
+  const int cnt = min(CH, T.first[t] + T.count[t] - p0);
 
   // ---- scores.  B operand: column n = lane % 16 is query head 8 g + n / 2
   // (n even: the query's high bf16 part, odd: the middle part); a second B
@@ -98,14 +108,14 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
       bl[s] = make_uint4(pack2(wl[0], wl[1]), pack2(wl[2], wl[3]), pack2(wl[4], wl[5]), pack2(wl[6], wl[7]));
     }
   }
-  // A operand: row = position 64 wave + 16 b + lane % 16 of the chunk; its
+  // A operand: row = position CH / 4 wave + 16 b + lane % 16 of the chunk; its
   // key row is 256 contiguous bytes (rows past the chunk's end read an
   // in-ring row and are masked below)
   const float scale = 0.08838834764831845f;   // 1 / sqrt(128), exact to fp32 rounding
-  uint4 ka[4][4];
+  uint4 ka[BW][4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int j = 64 * wave + 16 * b + (lane & 15);
+  for (int b = 0; b < BW; ++b) {
+    const int j = 16 * BW * wave + 16 * b + (lane & 15);
     const uint4* kr = reinterpret_cast<const uint4*>(k + ((size_t)((p0 + j) % ring) * AKV + g) * AD);
 #pragma unroll
     for (int s = 0; s < 4; ++s) ka[b][s] = kr[4 * s + (lane >> 4)];
@@ -113,22 +123,22 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   // the chunk's value rows: 8 threads per 256-byte row, 32 bytes each (rows
   // past the chunk's end repeat its first row), all requested now and written
   // to LDS after the scores
-  uint4 vst[8];
+  uint4 vst[CH / 32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < CH / 32; ++i) {
     const int j = 32 * i + (tid >> 3), piece = tid & 7;   // rows 32 i .. 32 i + 31
     const int jj = j < cnt ? j : 0;
     vst[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece];
   }
-  uint4 vst2[8];
+  uint4 vst2[CH / 32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < CH / 32; ++i) {
     const int j = 32 * i + (tid >> 3), piece = tid & 7;
     const int jj = j < cnt ? j : 0;
     vst2[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece + 1];
   }
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < BW; ++b) {
     at_f32x4 d = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -140,12 +150,12 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     for (int r = 0; r < 4; ++r) {
       const float other = dpp_f32<DPP_XOR1>(d[r]);
       const float sum = ((lane & 1) ? other + d[r] : d[r] + other) + e[r];   // hi + mid, then + lo
-      const int j = 64 * wave + 16 * b + 4 * (lane >> 4) + r;
+      const int j = 16 * BW * wave + 16 * b + 4 * (lane >> 4) + r;
       if ((lane & 1) == 0) s_lds[j][(lane & 15) >> 1] = j < cnt ? sum * scale : -INFINITY;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < CH / 32; ++i) {
     const int j = 32 * i + (tid >> 3), piece = tid & 7;
     uint2* row = reinterpret_cast<uint2*>(&v_lds[j][0]) + 4 * piece;
     row[0] = make_uint2(vst[i].x, vst[i].y);
@@ -157,11 +167,14 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
 
   // ---- per head: chunk maximum, e^(s - m) and their sum (thread = position)
   float sv[AG], m[AG];
-  {
+  if (tid < CH) {
     const float4 s0 = *reinterpret_cast<const float4*>(&s_lds[tid][0]);
     const float4 s1 = *reinterpret_cast<const float4*>(&s_lds[tid][4]);
     sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
     sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+  } else {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) sv[h] = -INFINITY;   // threads past the chunk
   }
 #pragma unroll
   for (int h = 0; h < AG; ++h) {
@@ -181,8 +194,10 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   for (int h = 0; h < AG; ++h) {
     ev[h] = tid < cnt ? expf(sv[h] - m[h]) : 0.f;
     const uint32_t hi = f32_to_bf16_rne(ev[h]);
-    p16[2 * h][tid] = (uint16_t)hi;
-    p16[2 * h + 1][tid] = (uint16_t)f32_to_bf16_rne(ev[h] - bf16_bits_to_f32(hi));
+    if (tid < CH) {
+      p16[2 * h][tid] = (uint16_t)hi;
+      p16[2 * h + 1][tid] = (uint16_t)f32_to_bf16_rne(ev[h] - bf16_bits_to_f32(hi));
+    }
   }
   __syncthreads();   // red is reused below; p16 holds the weights (the scores were read before the last barrier)
   float lsum[AG];
@@ -198,11 +213,11 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   // ---- weighted values on the matrix cores: O^T[d][2 h + part] =
   // sum_p V[p][d] P16[2 h + part][p] (A: 16 dimensions x 32 positions, the
   // value column gathered from LDS; B: 32 positions x 16 weight rows), all
-  // 256 positions in 8 steps; O[h][d] = part 0 + part 1.  Wave w takes the
+  // CH positions in CH / 32 steps; O[h][d] = part 0 + part 1.  Wave w takes the
   // dimensions 32 w .. 32 w + 31 (two blocks of 16).
   at_f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int st = 0; st < ACH / 32; ++st) {
+  for (int st = 0; st < CH / 32; ++st) {
     const int kb = 32 * st + 8 * (lane >> 4);
     const uint4 bp = *reinterpret_cast<const uint4*>(&p16[lane & 15][kb]);
 #pragma unroll
@@ -302,7 +317,9 @@ __global__ void __launch_bounds__(ACD * ACS) k_attn_combine(const float* __restr
 }
 
 size_t attn_workspace_bytes(int n_tokens, int max_seen) {
-  const size_t nch = (size_t)(max_seen + ACH - 1) / ACH;
+  // chunks of the longer of: ACH positions, or ACH_S positions up to ACH_SMAX seen
+  const size_t nch = std::max<size_t>((size_t)(max_seen + ACH - 1) / ACH,
+                                      (size_t)(std::min(max_seen, ACH_SMAX) + ACH_S - 1) / ACH_S);
   return (size_t)n_tokens * AQ * nch * APART * sizeof(float);
 }
 
@@ -310,14 +327,21 @@ hipError_t launch_attn_decode(const float* q, const uint16_t* k, const uint16_t*
                               const int* first, const int* count, int n_tokens, float* out, float* ws,
                               hipStream_t s) {
   AttnTokens T = {};
-  int nch_max = 0;
+  int nch_max = 0, nch_big = 0, nch_small = 0;
   for (int t = 0; t < n_tokens; ++t) {
     T.first[t] = first[t];
     T.count[t] = count[t];
-    T.nch[t] = (count[t] + ACH - 1) / ACH;
+    T.chunk[t] = count[t] <= ACH_SMAX ? ACH_S : ACH;   // by the token's own range only
+    T.nch[t] = (count[t] + T.chunk[t] - 1) / T.chunk[t];
     nch_max = max(nch_max, T.nch[t]);
+    if (T.chunk[t] == ACH) nch_big = max(nch_big, T.nch[t]);
+    else nch_small = max(nch_small, T.nch[t]);
   }
-  hipLaunchKernelGGL(k_attn_chunk, dim3(nch_max, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max, ws);
+  if (nch_big)
+    hipLaunchKernelGGL(k_attn_chunk<ACH>, dim3(nch_big, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max, ws);
+  if (nch_small)
+    hipLaunchKernelGGL(k_attn_chunk<ACH_S>, dim3(nch_small, AKV, n_tokens), dim3(ANT), 0, s, q, k, v, ring, T, nch_max,
+                       ws);
   hipLaunchKernelGGL(k_attn_combine, dim3(AQ, AD / ACD, n_tokens), dim3(ACD * ACS), 0, s, sinks, T, nch_max, ws, out);
   return hipGetLastError();
 }

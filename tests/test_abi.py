@@ -53,7 +53,10 @@ def test_attention_rejects_bad_arguments_before_any_hip_call():
     lib = F.lib()
     A = 16   # any non-null, 16-byte aligned address: validation fails before it is used
     ws = F.flint_attn_workspace_bytes(1, 513)
-    assert ws == 1 * 32 * 3 * 132 * 4     # 3 chunks of 256 positions, 132 floats per head
+    assert ws == 1 * 32 * 9 * 132 * 4     # 9 chunks of 64 positions, 132 floats per head
+    assert F.flint_attn_workspace_bytes(1, 768) == 1 * 32 * 12 * 132 * 4
+    assert F.flint_attn_workspace_bytes(2, 769) == 2 * 32 * 12 * 132 * 4   # 4 chunks of 256, or 12 of 64 for others
+    assert F.flint_attn_workspace_bytes(1, 100000) == 1 * 32 * 391 * 132 * 4
     assert F.flint_attn_workspace_bytes(0, 513) == 0 and F.flint_attn_workspace_bytes(17, 513) == 0
     assert F.flint_attn_workspace_bytes(1, 0) == 0
     inval = F.FLINT_ERR_INVALID_ARG

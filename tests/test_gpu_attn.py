@@ -9,7 +9,8 @@ logits U(-9.0, 12.4) in bf16 (the checkpoint's range).
 Bound: scores are exact products summed in fp32 inside the matrix cores (the
 query in three bf16 parts), so their error is a few fp32 ulps of the sum of
 |q_i k_i| / sqrt(128) (about 1e-6 absolute).  The sums of e^(s - m) and of
-e^(s - m) v are fp32 in a fixed order over at most 256 positions per chunk and
+e^(s - m) v are fp32 in a fixed order over at most 256 positions per chunk (64
+for a token that sees at most 768) and
 then over the chunks: relative error at most (256 + chunks) 2^-24, 4e-5 at
 100,000 positions, typically far less.  1e-4 relative L2 per token still fails
 a wrong head group, a dropped sink, a wrong scale or a window off by one
@@ -61,12 +62,12 @@ def check(q, kb, vb, sinks, pos, window, out):
 
 def test_window_layer_positions_and_chunk_edges():
     """Window layer, ring of 640 rows: the first positions (fewer than 513
-    visible), the chunk edges 256 / 257 / 512 / 513 visible, and positions far
-    past the ring's first wrap; all in one call of 10 tokens."""
+    visible), the chunk edges 64 / 65 / 256 / 257 / 512 / 513 visible, and
+    positions far past the ring's first wrap; all in one call of 12 tokens."""
     ring, W = fg.ATT_RING, fg.ATT_WINDOW
     kb, vb = fg.attn_cache(0, 1, ring)
     sinks = fg.attn_sinks(0, 1)
-    pos = [0, 1, 100, 255, 256, 511, 512, 639, 1000, 70000]
+    pos = [0, 1, 63, 64, 100, 255, 256, 511, 512, 639, 1000, 70000]
     q = fg.attn_queries(0, 1, len(pos))
     out = run_attn(q, kb, vb, sinks, pos, W, ring)
     errs = check(q, kb, vb, sinks, pos, W, out)
@@ -83,6 +84,23 @@ def test_full_layer_long_context(n_pos):
     out = run_attn(q, kb, vb, sinks, pos, 0, n_pos)
     errs = check(q, kb, vb, sinks, pos, 0, out)
     print(f"full layer, {n_pos} positions: rel-L2 max {max(errs):.2e}")
+
+
+def test_chunk_size_switch():
+    """Tokens seeing at most 768 positions are cut into chunks of 64, longer
+    ones into chunks of 256: both sides of the switch (768 / 769 visible) and
+    of the chunk edges, in one call and each alone (bitwise)."""
+    n_pos = 2048
+    kb, vb = fg.attn_cache(0, 6, n_pos)
+    sinks = fg.attn_sinks(0, 6)
+    pos = [0, 63, 64, 127, 766, 767, 768, 769, 1023, 1024, 2047]
+    q = fg.attn_queries(0, 6, len(pos))
+    out = run_attn(q, kb, vb, sinks, pos, 0, n_pos)
+    for t in range(len(pos)):
+        alone = run_attn(q[t:t + 1], kb, vb, sinks, pos[t:t + 1], 0, n_pos)
+        assert np.array_equal(alone[0], out[t]), t
+    errs = check(q, kb, vb, sinks, pos, 0, out)
+    print(f"chunk size switch: rel-L2 max {max(errs):.2e}")
 
 
 def test_tokens_independent_and_deterministic():
