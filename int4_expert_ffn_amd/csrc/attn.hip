@@ -11,8 +11,8 @@
 //                   precision), the chunk's maximum, e^(s - m), their sum and
 //                   the weighted sum of the values, also on the matrix cores
 //                   (the weights as two bf16 parts) -> one partial per head
-//   k_attn_combine  per (query head, 32 dimensions, token): the partials and
-//                   the sink in a fixed order (8 interleaved subsets of the
+//   k_attn_combine  per (query head, 16 dimensions, token): the partials and
+//                   the sink in a fixed order (16 interleaved subsets of the
 //                   chunks, each in chunk order, then the subsets in order)
 //                   -> out
 // Each token's chunks are computed the same way whatever the other tokens
@@ -57,14 +57,16 @@ struct AttnTokens {
 };
 constexpr int ACH_S = 64, ACH_SMAX = 768;
 
-// CH positions per workgroup (a multiple of 64): wave w scores positions
-// 64 w' + 16 b of the chunk for its CH / 64 blocks; tokens whose chunk size is
-// not CH are left to the other instance.
+// CH positions per chunk (a multiple of 64): wave w scores positions
+// CH / 4 w + 16 b of the chunk for its CH / 64 blocks.  Workgroup (c, g, t)
+// takes chunk c of token t and KV head g; tokens whose chunk size is not CH
+// are left to the other instance.
 template <int CH>
 __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q, const uint16_t* __restrict__ k,
                                                     const uint16_t* __restrict__ v, int ring, AttnTokens T, int nch_max,
                                                     float* __restrict__ ws) {
-  constexpr int BW = CH / 64;   // blocks of 16 positions per wave (CH / 4 positions per wave)
+  constexpr int BW = CH / 64;   // blocks of 16 positions per wave
+  constexpr int NV = CH / 32;   // value loads per thread and half row
   // scores [position][head]; once they are in registers the same memory holds
   // e^(s - m) as two bf16 parts [2 h + part][position]
   __shared__ __align__(16) float sp_lds[CH * AG];
@@ -75,24 +77,69 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
   // the chunk's value rows of this KV head, rows padded to 264 bytes so that
   // the matrix-core operand reads (16 dimensions x rows 8 apart) hit distinct banks
   __shared__ __align__(16) uint16_t v_lds[CH][AVP];
-  const int t = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
-  if (T.chunk[t] != CH || c >= T.nch[t]) return;
+  const int t = blockIdx.z, g = blockIdx.y;
+  if (T.chunk[t] != CH) return;
+  const int nch = T.nch[t], first = T.first[t], last = T.first[t] + T.count[t];
+  const int c = blockIdx.x;
+  if (c >= nch) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int p0 = T.first[t] + c * CH;
-  const int cnt = min(CH, T.first[t] + T.count[t] - p0);
 
-  // ---- scores.  B operand: column n = lane % 16 is query head 8 g + n / 2
-  // (n even: the query's high bf16 part, odd: the middle part); a second B
-  // carries the low part in the even columns.  q = hi + mid + lo exactly.
-  uint4 bq[4], bl[4];
+  // ---- the chunk's keys and values into registers.  Keys: the A operand, row =
+  // position CH / 4 wave + 16 b + lane % 16 of the chunk, 256 contiguous bytes
+  // (rows past the chunk's end read an in-ring row and are masked below).
+  // Values: 8 threads per 256-byte row, 32 bytes each (rows past the chunk's
+  // end repeat its first row), written to LDS after the scores.
+  const int p0 = first + c * CH, cnt = min(CH, last - p0);
+  uint4 ka[BW][4], vst[NV], vst2[NV];
+  auto load_keys = [&]() {
+#pragma unroll
+    for (int b = 0; b < BW; ++b) {
+      const int j = 16 * BW * wave + 16 * b + (lane & 15);
+      const uint4* kr = reinterpret_cast<const uint4*>(k + ((size_t)((p0 + j) % ring) * AKV + g) * AD);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[b][s] = kr[4 * s + (lane >> 4)];
+    }
+  };
+  auto load_values = [&]() {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = 32 * i + (tid >> 3), piece = tid & 7;   // rows 32 i .. 32 i + 31
+      const int jj = j < cnt ? j : 0;
+      vst[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int j = 32 * i + (tid >> 3), piece = tid & 7;
+      const int jj = j < cnt ? j : 0;
+      vst2[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece + 1];
+    }
+  };
+  // ---- B operands of the scores.  Column n = lane % 16 is query head
+  // 8 g + n / 2 (n even: the query's high bf16 part, odd: the middle part); a
+  // second B carries the low part in the even columns.  q = hi + mid + lo exactly.
+  // The keys are requested before the query and the values after it (loads
+  // return in order: the query's wait covers the keys only).
+  load_keys();
+  float4 qv[8];
   {
-    const int n = lane & 15, h = AG * g + (n >> 1), odd = n & 1;
-    const float* qh = q + ((size_t)t * AQ + h) * AD;
+    const float* qh = q + ((size_t)t * AQ + AG * g + ((lane & 15) >> 1)) * AD + 8 * (lane >> 4);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int k0 = 32 * s + 8 * (lane >> 4);
-      const float4 x0 = *reinterpret_cast<const float4*>(qh + k0);
-      const float4 x1 = *reinterpret_cast<const float4*>(qh + k0 + 4);
+      qv[2 * s] = *reinterpret_cast<const float4*>(qh + 32 * s);
+      qv[2 * s + 1] = *reinterpret_cast<const float4*>(qh + 32 * s + 4);
+    }
+  }
+  load_values();
+  // keep the conversion below every load: the values must not wait for the keys
+  compiler_fence();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
+  uint4 bq[4], bl[4];
+  {
+    const int odd = lane & 1;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float4 x0 = qv[2 * s], x1 = qv[2 * s + 1];
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t w[8], wl[8];
 #pragma unroll
@@ -108,35 +155,8 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
       bl[s] = make_uint4(pack2(wl[0], wl[1]), pack2(wl[2], wl[3]), pack2(wl[4], wl[5]), pack2(wl[6], wl[7]));
     }
   }
-  // A operand: row = position CH / 4 wave + 16 b + lane % 16 of the chunk; its
-  // key row is 256 contiguous bytes (rows past the chunk's end read an
-  // in-ring row and are masked below)
   const float scale = 0.08838834764831845f;   // 1 / sqrt(128), exact to fp32 rounding
-  uint4 ka[BW][4];
-#pragma unroll
-  for (int b = 0; b < BW; ++b) {
-    const int j = 16 * BW * wave + 16 * b + (lane & 15);
-    const uint4* kr = reinterpret_cast<const uint4*>(k + ((size_t)((p0 + j) % ring) * AKV + g) * AD);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) ka[b][s] = kr[4 * s + (lane >> 4)];
-  }
-  // the chunk's value rows: 8 threads per 256-byte row, 32 bytes each (rows
-  // past the chunk's end repeat its first row), all requested now and written
-  // to LDS after the scores
-  uint4 vst[CH / 32];
-#pragma unroll
-  for (int i = 0; i < CH / 32; ++i) {
-    const int j = 32 * i + (tid >> 3), piece = tid & 7;   // rows 32 i .. 32 i + 31
-    const int jj = j < cnt ? j : 0;
-    vst[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece];
-  }
-  uint4 vst2[CH / 32];
-#pragma unroll
-  for (int i = 0; i < CH / 32; ++i) {
-    const int j = 32 * i + (tid >> 3), piece = tid & 7;
-    const int jj = j < cnt ? j : 0;
-    vst2[i] = reinterpret_cast<const uint4*>(v + ((size_t)((p0 + jj) % ring) * AKV + g) * AD)[2 * piece + 1];
-  }
+  // ---- scores
 #pragma unroll
   for (int b = 0; b < BW; ++b) {
     at_f32x4 d = {0.f, 0.f, 0.f, 0.f}, e = {0.f, 0.f, 0.f, 0.f};
@@ -155,7 +175,7 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     }
   }
 #pragma unroll
-  for (int i = 0; i < CH / 32; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int j = 32 * i + (tid >> 3), piece = tid & 7;
     uint2* row = reinterpret_cast<uint2*>(&v_lds[j][0]) + 4 * piece;
     row[0] = make_uint2(vst[i].x, vst[i].y);
@@ -163,7 +183,7 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     row[2] = make_uint2(vst2[i].x, vst2[i].y);
     row[3] = make_uint2(vst2[i].z, vst2[i].w);
   }
-  __syncthreads();
+  wg_sync();
 
   // ---- per head: chunk maximum, e^(s - m) and their sum (thread = position)
   float sv[AG], m[AG];
@@ -186,7 +206,7 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     x = fmaxf(fmaxf(lane_bcast(x, 0), lane_bcast(x, 16)), fmaxf(lane_bcast(x, 32), lane_bcast(x, 48)));
     if (lane == 0) red[wave][h] = x;
   }
-  __syncthreads();
+  wg_sync();
 #pragma unroll
   for (int h = 0; h < AG; ++h) m[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
   float ev[AG];
@@ -199,22 +219,22 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
       p16[2 * h + 1][tid] = (uint16_t)f32_to_bf16_rne(ev[h] - bf16_bits_to_f32(hi));
     }
   }
-  __syncthreads();   // red is reused below; p16 holds the weights (the scores were read before the last barrier)
+  wg_sync();   // red is reused below; p16 holds the weights (the scores were read before the last barrier)
   float lsum[AG];
 #pragma unroll
   for (int h = 0; h < AG; ++h) {
     const float x = wave_sum(ev[h]);   // fixed tree
     if (lane == 0) red[wave][h] = x;
   }
-  __syncthreads();
+  wg_sync();
 #pragma unroll
   for (int h = 0; h < AG; ++h) lsum[h] = ((red[0][h] + red[1][h]) + red[2][h]) + red[3][h];
 
   // ---- weighted values on the matrix cores: O^T[d][2 h + part] =
   // sum_p V[p][d] P16[2 h + part][p] (A: 16 dimensions x 32 positions, the
   // value column gathered from LDS; B: 32 positions x 16 weight rows), all
-  // CH positions in CH / 32 steps; O[h][d] = part 0 + part 1.  Wave w takes the
-  // dimensions 32 w .. 32 w + 31 (two blocks of 16).
+  // CH positions in CH / 32 steps; O[h][d] = part 0 + part 1.  Wave w takes
+  // the dimensions 32 w .. 32 w + 31 (two blocks of 16).
   at_f32x4 o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int st = 0; st < CH / 32; ++st) {
@@ -225,19 +245,27 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
       const int dd = 32 * wave + 16 * db + (lane & 15);
       uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)v_lds[kb + 2 * i][dd] | ((uint32_t)v_lds[kb + 2 * i + 1][dd] << 16);
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)v_lds[kb + 2 * i][dd] | ((uint32_t)v_lds[kb + 2 * i + 1][dd] << 16);
       o[db] = mfma16(make_uint4(w[0], w[1], w[2], w[3]), bp, o[db]);
     }
   }
-  // ---- partials: lanes with an even column hold head (lane % 16) / 2
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
+  // ---- partials: lanes 2 n and 2 n + 1 hold the two weight parts of head
+  // n for the dimensions 32 wave + 16 db + 4 (lane / 16) .. + 3; both form
+  // the sum (the same value), the even lane stores block db = 0 and the odd
+  // lane db = 1, 16 bytes each
+  {
+    float4 res;
+    const int db = lane & 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float other = dpp_f32<DPP_XOR1>(o[db][r]);
-      const int h = (lane & 15) >> 1, dd = 32 * wave + 16 * db + 4 * (lane >> 4) + r;
-      if ((lane & 1) == 0) ws[(((size_t)t * AQ + AG * g + h) * nch_max + c) * APART + 4 + dd] = o[db][r] + other;
+      const float s0 = o[0][r] + dpp_f32<DPP_XOR1>(o[0][r]);
+      const float s1 = o[1][r] + dpp_f32<DPP_XOR1>(o[1][r]);
+      (&res.x)[r] = db ? s1 : s0;
     }
+    const int h = (lane & 15) >> 1, dd = 32 * wave + 16 * db + 4 * (lane >> 4);
+    *reinterpret_cast<float4*>(ws + (((size_t)t * AQ + AG * g + h) * nch_max + c) * APART + 4 + dd) = res;
+  }
 #pragma unroll
   for (int h = 0; h < AG; ++h)
     if (tid == h) {
@@ -247,13 +275,13 @@ __global__ void __launch_bounds__(ANT) k_attn_chunk(const float* __restrict__ q,
     }
 }
 
-// One workgroup per (query head, 32 dimensions, token): 32 dimensions x 8
+// One workgroup per (query head, 16 dimensions, token): 16 dimensions x 16
 // chunk subsets.  M = max(o, m_c) over the chunks (exact);
 // f_c = e^(m_c - M); L = e^(o - M) + sum_c l_c f_c and O = sum_c acc_c f_c,
-// each subset summing its chunks c = sub, sub + 8, ... in order, then the 8
+// each subset summing its chunks c = sub, sub + 16, ... in order, then the 16
 // subsets in order.
-constexpr int ACS = 8;          // chunk subsets
-constexpr int ACD = AD / 4;     // dimensions per workgroup
+constexpr int ACS = 16;         // chunk subsets
+constexpr int ACD = AD / 8;     // dimensions per workgroup
 __global__ void __launch_bounds__(ACD * ACS) k_attn_combine(const float* __restrict__ sinks, AttnTokens T,
                                                             int nch_max, const float* __restrict__ ws,
                                                             float* __restrict__ out) {
