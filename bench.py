@@ -46,6 +46,7 @@ TOKEN_BYTES = N_LAYERS * LAYER_BYTES                           # 659,209,216
 KERNEL_SOURCES = {
     "decode": ("decode_persistent.hip", "decode_persistent.h", "decode_common.h", "decode.h", "flint_device.h"),
     "head": ("dense.hip", "dense.h", "flint_device.h"),
+    "attn": ("attn.hip", "attn.h", "flint_device.h"),
 }
 
 
@@ -101,18 +102,28 @@ def _counter_values(run_dir, counter, name_pattern=None):
 HEAD_KERNEL = "k_rows_mfma"
 HEAD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_kernel_traffic.txt")
 HEAD_BYTES = 150144 * (H // 2) + 150144 * (H // G) * 2                # 158,552,064
+ATT_KERNEL = "k_attn_chunk"
+ATT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_chunk_traffic.txt")
+ATT_POSITIONS = 100000
+ATT_BYTES_PER_POS = 2 * 4 * 128 * 2        # k and v rows of the 4 KV heads, bf16
+# one batch-1 full-layer call: the cache, q, out and the sinks
+ATT_CALL_BYTES = ATT_POSITIONS * ATT_BYTES_PER_POS + 2 * 32 * 128 * 4 + 32 * 4   # 204,832,896
 
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands, which="decode"):
     """Write the traffic summary from four rocprofv3 --pmc runs: the benchmark
     (FETCH_SIZE, WRITE_SIZE, KiB per dispatch of its dominant kernel) and a
     plain 1 GiB device copy (the same two counters) that calibrates them.
-    which: "decode" (47-layer decode launch) or "head" (output head launch)."""
+    which: "decode" (47-layer decode launch), "head" (output head launch) or
+    "attn" (the chunk kernel of a batch-1 full attention layer)."""
     kernel, out_file, algo, title = {
         "decode": (DECODE_KERNEL, TRAFFIC_FILE, TOKEN_BYTES,
                    "# HBM traffic of one decode launch (47-layer Flint MoE stack, batch 1, the bench workload)"),
         "head": (HEAD_KERNEL, HEAD_TRAFFIC_FILE, HEAD_BYTES,
                  "# HBM traffic of one output-head launch (150,144 x 2,048 int4, bench.py --head-dense workload)"),
+        "attn": (ATT_KERNEL, ATT_TRAFFIC_FILE, ATT_CALL_BYTES,
+                 "# HBM traffic of one attention chunk launch (full layer, 100,000 positions, 1 token; "
+                 "bench.py --attn --attn-batch1 workload; the algorithmic bytes are the whole call's)"),
     }[which]
     def one(d, counter, pattern):
         vals = _counter_values(d, counter, pattern)
@@ -381,9 +392,6 @@ def bench_head_dense(args):
     print(json.dumps(out), flush=True)
 
 
-ATT_BYTES_PER_POS = 2 * 4 * 128 * 2        # k and v rows of the 4 KV heads, bf16
-
-
 def bench_attn(args):
     """Decode attention with learned sinks: a full layer at 100,000 positions
     (the recipe's 100K decode context) for 1, 4 and 16 query tokens at
@@ -394,7 +402,7 @@ def bench_attn(args):
     import flintgen as fg
     import int4_expert_ffn_amd as F
     dev = torch.device("cuda:0")
-    n_pos = 100000
+    n_pos = ATT_POSITIONS
     caches = []
     for i in range(2):
         kb, vb = fg.attn_cache(0, 10 + i, n_pos)
@@ -434,7 +442,7 @@ def bench_attn(args):
     res_full = {n: timed(full(n)) for n in ((1,) if args.attn_batch1 else (1, 4, 16))}
     res_win = {} if args.attn_batch1 else {n: timed(window(n)) for n in (1, 16)}
     med, mean = res_full[1][0], res_full[1][1]
-    algo = n_pos * ATT_BYTES_PER_POS + 2 * 32 * 128 * 4 + 32 * 4
+    algo = ATT_CALL_BYTES
     achieved = algo / mean / 1e9
     outj = {
         "metric": "decode attention with sinks, achieved HBM GB/s (full layer, 100,000 positions, batch 1)",
@@ -446,7 +454,10 @@ def bench_attn(args):
                                "640-row ring), 32 query / 4 KV heads of 128", "positions": n_pos,
                    "algorithmic_bytes_batch1": algo},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_from_profiles(ATT_TRAFFIC_FILE, "attn"),
+                     "traffic_note": "HBM bytes of the chunk kernel alone (rocprofv3 counters); the combine adds the "
+                                     "partials' read",
                      "kernel": "k_attn_chunk + k_attn_combine (one call, hip events; mean duration)"},
         "full_layer_us": {str(n): [round(v * 1e6, 2) for v in (r[0], r[2], r[3])] for n, r in res_full.items()},
         "window_layer_us": {str(n): [round(v * 1e6, 2) for v in (r[0], r[2], r[3])] for n, r in res_win.items()},
@@ -602,7 +613,7 @@ def main():
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the traffic summary under profiles/ from four rocprofv3 --pmc output folders")
     ap.add_argument("--command", action="append", default=[], help="command lines recorded in the summary")
-    ap.add_argument("--counters-kernel", choices=("decode", "head"), default="decode",
+    ap.add_argument("--counters-kernel", choices=("decode", "head", "attn"), default="decode",
                     help="which kernel --counters-summary summarises")
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill path instead: one layer, a 2048-token chunk")

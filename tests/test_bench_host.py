@@ -27,6 +27,8 @@ def test_algorithmic_bytes_match_the_block_shapes():
     assert bench.TOKEN_BYTES == 47 * 14025728 == 659209216
     assert bench.HEAD_BYTES == 150144 * (1024 + 32)
     assert bench.ATT_BYTES_PER_POS == 2048
+    # one batch-1 full attention layer: 100,000 positions of k and v, q and out in fp32, 32 sinks
+    assert bench.ATT_CALL_BYTES == 100000 * 2048 + 2 * 32 * 128 * 4 + 32 * 4 == 204832896
 
 
 def test_traffic_summary_only_counts_for_its_own_sources(tmp_path):
@@ -34,6 +36,7 @@ def test_traffic_summary_only_counts_for_its_own_sources(tmp_path):
     p.write_text(f"kernel_source_hash: {bench.kernel_source_hash('decode')}\nhbm_bytes_per_launch: 1234\n")
     assert bench.traffic_from_profiles(str(p), "decode") == 1234
     assert bench.traffic_from_profiles(str(p), "head") is None          # another kernel's sources
+    assert bench.traffic_from_profiles(str(p), "attn") is None
     p.write_text("kernel_source_hash: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
     assert bench.traffic_from_profiles(str(p), "decode") is None
     assert bench.traffic_from_profiles(str(tmp_path / "missing.txt")) is None
