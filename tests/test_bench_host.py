@@ -40,3 +40,15 @@ def test_traffic_summary_only_counts_for_its_own_sources(tmp_path):
     p.write_text("kernel_source_hash: 0000000000000000\nhbm_bytes_per_launch: 1234\n")
     assert bench.traffic_from_profiles(str(p), "decode") is None
     assert bench.traffic_from_profiles(str(tmp_path / "missing.txt")) is None
+
+
+def test_prefill_roofline_takes_the_binding_roof():
+    flops = sum(bench.prefill_flops(2048).values())
+    moved = bench.ROUTER_BYTES + 256 * bench.EXPERT_BYTES + bench.SHARED_BYTES + 2 * 2048 * 2048 * 4
+    r = bench.prefill_roofline(flops, moved, 450e-6)
+    # 453 MB at 8 TB/s (56.6 us) outlasts 105 GFLOP at 2.5 PFLOP/s (42.1 us)
+    assert r["bound"] == "hbm" and r["other_roof"]["bound"] == "mfma"
+    assert abs(r["achieved"] - moved / 450e-6 / 1e9) < 0.1
+    assert r["us_at_peak"]["hbm"] > r["us_at_peak"]["mfma"]
+    r2 = bench.prefill_roofline(flops * 4, moved, 450e-6)     # four times the flops: the matrix cores bind
+    assert r2["bound"] == "mfma" and r2["other_roof"]["bound"] == "hbm"
