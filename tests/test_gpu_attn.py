@@ -145,3 +145,32 @@ def test_verify_block_tokens_independent(n_pos):
         assert np.array_equal(alone[0], out[t]), t
     errs = check(q[[0, 14, 15]], kb, vb, sinks, [pos[0], pos[14], pos[15]], 0, out[[0, 14, 15]])
     print(f"verify block, {n_pos} positions: rel-L2 max {max(errs):.2e}")
+
+
+def test_writes_stay_inside_workspace_and_out():
+    """The call writes nothing past flint_attn_workspace_bytes(n, max_seen) nor
+    past out[n]: guard regions after both keep their sentinel, for a window
+    call, a mixed call (64- and 256-position chunks) and a long full layer."""
+    dev = torch.device("cuda")
+    sentinel = 0x7FA5A5A5   # a NaN pattern the kernels never write
+    cases = [(fg.ATT_RING, fg.ATT_WINDOW, [5000]), (4096, 0, [100, 700, 769, 4095]), (100000, 0, [99999])]
+    for ring, window, pos in cases:
+        kb, vb = fg.attn_cache(0, 7, ring)
+        sinks = fg.attn_sinks(0, 7)
+        q = fg.attn_queries(0, 7, len(pos))
+        n = len(pos)
+        max_seen = max((p - max(0, p - window + 1) + 1) if window else p + 1 for p in pos)
+        wsb = F.flint_attn_workspace_bytes(n, max_seen)
+        guard = 4096
+        ws = torch.full((wsb // 4 + guard,), sentinel, dtype=torch.int32, device=dev)
+        out = torch.full((n * 32 * 128 + guard,), sentinel, dtype=torch.int32, device=dev)
+        qd = torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(dev)
+        kd = torch.from_numpy(np.ascontiguousarray(kb)).to(dev)
+        vd = torch.from_numpy(np.ascontiguousarray(vb)).to(dev)
+        sd = torch.from_numpy(np.ascontiguousarray(sinks, np.float32)).to(dev)
+        F.flint_attn_decode(qd, kd, vd, ring, sd, pos, n, window, out, ws, wsb)
+        torch.cuda.synchronize()
+        assert bool((ws[wsb // 4:] == sentinel).all()), (ring, window, pos)
+        assert bool((out[n * 32 * 128:] == sentinel).all()), (ring, window, pos)
+        res = out[: n * 32 * 128].view(torch.float32).view(n, 32, 128).cpu().numpy()
+        check(q, kb, vb, sinks, pos, window, res)
