@@ -217,3 +217,19 @@ def test_single_token_exchange_slots_across_mixed_calls(model):
             assert torch.equal(a, b), (i, calls[i])
     finally:
         ref.close()
+
+
+def test_writes_stay_inside_out(model):
+    """flint_moe_forward writes n_tokens x 2048 floats of out and nothing past
+    them (a guard region keeps its sentinel): the one-token kernel, a token-group
+    call and the largest decode batch; the values equal an ordinary call's."""
+    synth, m, ids, w = model
+    sentinel = 0x7FA5A5A5   # a NaN pattern the kernels never write
+    for n in (1, 5, CAP):
+        x = torch.from_numpy(fg.tokens(11, range(n))).cuda()
+        out = torch.full((n * FL.hidden + 4096,), sentinel, dtype=torch.int32, device="cuda")
+        F.flint_moe_forward(m.h, x, n, 0, N_LAYERS, out, None)
+        ref = m.forward(x)
+        torch.cuda.synchronize()
+        assert bool((out[n * FL.hidden:] == sentinel).all()), n
+        assert torch.equal(out[: n * FL.hidden].view(torch.float32).view(n, FL.hidden), ref), n

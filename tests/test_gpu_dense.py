@@ -147,3 +147,28 @@ def test_dense_mlp_power_of_two_up_scale_is_exact(dense):
     w2 = dict(w, up_s=(w["up_s"].to(torch.int32) + (3 << 7)).to(torch.int16))
     h2, _ = run_dense(inter, w2, x)
     assert np.array_equal(h2, h * 8.0)
+
+
+def test_writes_stay_inside_outputs(head, dense):
+    """The head writes n x rows logits and the dense MLP n x inter of h and
+    n x 2048 of out, nothing past them (guard regions keep their sentinel),
+    with a ragged row count for the head."""
+    sentinel = 0x7FA5A5A5
+    c, s = head
+    x = torch.from_numpy(fg.tokens(13, range(3))).cuda()
+    rows = 1000
+    logits = torch.full((3 * rows + 4096,), sentinel, dtype=torch.int32, device="cuda")
+    F.flint_head_forward(F.q4(c, s), rows, x, 3, logits)
+    torch.cuda.synchronize()
+    assert bool((logits[3 * rows:] == sentinel).all())
+    inter, w, wc = dense
+    h = torch.full((3 * inter + 4096,), sentinel, dtype=torch.int32, device="cuda")
+    out = torch.full((3 * H + 4096,), sentinel, dtype=torch.int32, device="cuda")
+    F.flint_dense_mlp_forward(F.q4(w["gate"], w["gate_s"]), F.q4(w["up"], w["up_s"]), F.q4(w["down"], w["down_s"]),
+                              inter, x, 3, h, out)
+    torch.cuda.synchronize()
+    assert bool((h[3 * inter:] == sentinel).all())
+    assert bool((out[3 * H:] == sentinel).all())
+    h_ref, out_ref = run_dense(inter, w, x.cpu().numpy())
+    assert np.array_equal(h[: 3 * inter].view(torch.float32).view(3, inter).cpu().numpy(), h_ref)
+    assert np.array_equal(out[: 3 * H].view(torch.float32).view(3, H).cpu().numpy(), out_ref)

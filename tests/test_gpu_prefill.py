@@ -172,3 +172,19 @@ def test_prefill_scaled_up_projection(scaled):
         hmax = max(hmax, res.max_abs_h)
     print(f"max |h| {hmax:.3g}")
     assert hmax > 65504.0
+
+
+def test_writes_stay_inside_out(uniform):
+    """The prefill path writes n_tokens x 2048 floats of out and nothing past
+    them (a guard region keeps its sentinel), for a ragged 100-token call and
+    the full 2,048-token chunk; the values equal an ordinary call's."""
+    synth, m, ids, w = uniform
+    sentinel = 0x7FA5A5A5
+    for n in (100, NMAX):
+        x = torch.from_numpy(fg.tokens(12, range(n))).cuda()
+        out = torch.full((n * FL.hidden + 4096,), sentinel, dtype=torch.int32, device="cuda")
+        F.flint_moe_forward(m.h, x, n, 0, 1, out, None)
+        ref = m.forward(x)
+        torch.cuda.synchronize()
+        assert bool((out[n * FL.hidden:] == sentinel).all()), n
+        assert torch.equal(out[: n * FL.hidden].view(torch.float32).view(n, FL.hidden), ref), n
