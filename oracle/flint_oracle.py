@@ -29,7 +29,7 @@ sections; see also the readings listed below):
 * Intermediates stay in high precision: the pages report SwiGLU activations
   near 2.6e5 in the top layers, past fp16 (TandemLLM "21 Flint", 21.2).
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
 bias added after the sigmoid (c = s + b); routing weights from the unbiased s
 of the picks, normalised to sum 1 with no epsilon and no extra scale; shared
 expert added with weight 1; SiLU on the gate; exact ties in c go to the lower
