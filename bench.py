@@ -268,12 +268,13 @@ def bench_cost_table(args):
     """Verify-block cost table: one forward call of n = 1..16 independent tokens
     through the 47 layers (the decode path), median time per call.  Algorithmic
     bytes per call count each layer's router, shared expert and the distinct
-    routed experts the call's tokens picked (from the trace)."""
+    routed experts the call's tokens picked (from the trace).  --interm-div
+    gives the fp16-intermediate pack form of the same weights."""
     import torch
     import flintgen as fg
     import int4_expert_ffn_amd as F
     dev = torch.device("cuda:0")
-    model = build_stack_model(dev)
+    model = build_stack_model(dev, args.interm_div)
     cap = 16
     pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
     ids = torch.full((N_LAYERS, cap, K), -1, dtype=torch.int32, device=dev)
@@ -318,12 +319,15 @@ def bench_cost_table(args):
         print(f"n={n}: {rows[-1]}", file=sys.stderr, flush=True)
     if args.cost_table_out:
         with open(args.cost_table_out, "w") as f:
+            form = (f"fp16-intermediate form (routed up projections / {args.interm_div})" if args.interm_div
+                    else "fp32 intermediates")
             f.write("# Verify-block cost table: one flint_moe_forward call of n independent tokens through the\n"
-                    "# 47-layer stack (decode path), hip events on the launch stream, "
+                    f"# 47-layer stack (decode path, {form}), hip events on the launch stream, "
                     f"{args.steps} timed calls per n after {args.warmup} warm-up, 4 token batches per n in turn.\n"
                     "# bytes: router + shared + distinct routed experts per layer (from the trace), summed over layers.\n"
                     "# command: python bench.py --cost-table --steps "
-                    f"{args.steps} --warmup {args.warmup} --cost-table-out <file>\n")
+                    f"{args.steps} --warmup {args.warmup}"
+                    + (f" --interm-div {args.interm_div}" if args.interm_div else "") + " --cost-table-out <file>\n")
             f.write("n,us_median,us_p10,us_p90,tokens_per_s,distinct_experts_per_layer,algorithmic_bytes,gbps,frac_of_8tbs\n")
             for r in rows:
                 f.write(f"{r['n']},{r['us_median']},{r['us_p10']},{r['us_p90']},{r['tokens_per_s']},"
@@ -332,7 +336,8 @@ def bench_cost_table(args):
     print(json.dumps({"metric": "verify-block cost table (47-layer decode call time for n = 1..16 tokens)",
                       "unit": "us per call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic (seeded int4 weights, bf16 scales, N(0,1) tokens)",
-                      "config": {"workload": "47-layer Flint MoE block stack, n independent tokens per call"},
+                      "config": {"workload": "47-layer Flint MoE block stack, n independent tokens per call",
+                                 "interm_div": args.interm_div},
                       "table": rows}), flush=True)
 
 

@@ -101,9 +101,10 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
  * handle rounds the SwiGLU output of every expert (routed and shared) to fp16,
  * nearest even (overflow gives inf), before its down projection, and scales
  * the routed weights by interm_div in the combine.  It is implemented for
- * single-token calls (n_tokens == 1) on GPUs that run the persistent decode
- * kernel; other calls return FLINT_ERR_UNSUPPORTED.  interm_div = 0 is
- * flint_moe_create. */
+ * decode calls (1 <= n_tokens <= 16) on GPUs that run the persistent decode
+ * kernel, each token's result bitwise the same as running it alone; prefill
+ * calls (n_tokens > 16) and the per-layer decode mode return
+ * FLINT_ERR_UNSUPPORTED.  interm_div = 0 is flint_moe_create. */
 int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, int interm_div,
                                  flint_moe_t* out);
 

@@ -137,7 +137,7 @@ def flint_moe_create(layers) -> int:
 
 def flint_moe_create_fp16_interm(layers, interm_div) -> int:
     """Handle for weights whose routed up projections are divided by
-    ``interm_div``; SwiGLU outputs are rounded to fp16 (single-token calls)."""
+    ``interm_div``; SwiGLU outputs are rounded to fp16 (decode calls of up to 16 tokens)."""
     h = ctypes.c_void_p()
     _check(lib().flint_moe_create_fp16_interm(_layer_array(layers), len(layers), interm_div, ctypes.byref(h)))
     return h.value

@@ -26,7 +26,7 @@ struct PersistArgs {
   uint32_t* vh;            // [2][n_layers][TOPK*I + IS] h of each layer, workgroup-major
   int n_layers;            // layers of the handle (every one is re-armed)
   int parity;              // half of vx / vh that this call writes
-  float interm_mult;       // 0: fp32 SwiGLU outputs; else fp16 ones, routed weights times this (one token only)
+  float interm_mult;       // 0: fp32 SwiGLU outputs; else fp16 ones, routed weights times this
 };
 
 // Value of an exchange slot that has not been written in the current call (a

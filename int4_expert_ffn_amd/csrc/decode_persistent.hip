@@ -576,8 +576,10 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
 // exchanges carry one token and involve only its P workgroups, so their size
 // does not grow with n.  Every row is computed by the same device function
 // with the same reduction shape as in a single-token call, so each token's
-// result is bitwise the same as running it alone.
-template <int K>
+// result is bitwise the same as running it alone.  F16H: the fp16-intermediate
+// form, each SwiGLU output rounded to fp16 and the routed weights scaled by
+// A.interm_mult, as in the one-token kernel (one value per exchange word).
+template <int K, bool F16H>
 __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
   constexpr int P = NWG / K;
   constexpr int NSH = 4 * K, NRT = 12 * K, NTASK = NSH + NRT;   // gate/up row pairs of a workgroup
@@ -725,7 +727,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
           const int word = j < NSH ? TOPK * I + NSH * u + j : NRT * u + (j - NSH);   // slot * I + row
           const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
           if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
-            hloc[j] = hv;
+            hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
             hloc_idx[j] = word;
           }
         }
@@ -758,6 +760,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
         return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
                            : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
       };
+      float wsc[TOPK];   // fp16 form: routed weights times the pack's divisor
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) wsc[i] = F16H ? w_l[i] * A.interm_mult : 0.f;
       uint4 ca = ca0, cb = cb0;
       uint32_t sa = sa0, sb = sb0;
       for (int i = 0; i < K; ++i) {
@@ -765,7 +770,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
         uint4 nca = ca, ncb = cb;
         uint32_t nsa = sa, nsb = sb;
         if (i + 1 < K) load_down_row(L, ids_l, NOUT * u + lr + NWAVES, nca, nsa, ncb, nsb);
-        const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
+        float v;
+        if constexpr (F16H) v = down_row_token(ca, sa, cb, sb, load_a, load_b, wsc, xown[lr]);
+        else v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
         if (lane == 0) xnew[lr] = v;
         ca = nca; cb = ncb; sa = nsa; sb = nsb;
       }
@@ -794,8 +801,8 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
 // Its exchanges carry one token and involve only its P workgroups, so their
 // size does not grow with n.  Every row is computed by the same device
 // function with the same reduction shape as in a single-token call, so each
-// token's result is bitwise the same as running it alone.
-template <int K>
+// token's result is bitwise the same as running it alone.  F16H as above.
+template <int K, bool F16H>
 __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
   constexpr int MSH = 4 * K, MRT = 12 * K, MTASK = MSH + MRT;   // most gate/up row pairs of a workgroup
   constexpr int MOUT = 8 * K;                                   // most output rows of a workgroup
@@ -938,7 +945,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
           const int word = j < nsh ? TOPK * I + s0 + j : q0 + (j - nsh);   // slot * I + row
           const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
           if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
-            hloc[j] = hv;
+            hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
             hloc_idx[j] = word;
           }
         }
@@ -973,6 +980,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
       };
       // unrolled with a fixed bound: the prefetched codes are renamed, never
       // copied (a copy would wait for the load in flight)
+      float wsc[TOPK];   // fp16 form: routed weights times the pack's divisor
+#pragma unroll
+      for (int i = 0; i < TOPK; ++i) wsc[i] = F16H ? w_l[i] * A.interm_mult : 0.f;
       uint4 ca = ca0, cb = cb0;
       uint32_t sa = sa0, sb = sb0;
 #pragma unroll
@@ -982,7 +992,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
         uint4 nca = ca, ncb = cb;
         uint32_t nsa = sa, nsb = sb;
         if (lr + NWAVES < nout) load_down_row(L, ids_l, o0 + lr + NWAVES, nca, nsa, ncb, nsb);
-        const float v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
+        float v;
+        if constexpr (F16H) v = down_row_token(ca, sa, cb, sb, load_a, load_b, wsc, xown[lr]);
+        else v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
         if (lane == 0) xnew[lr] = v;
         ca = nca; cb = ncb; sa = nsa; sb = nsb;
       }
@@ -1003,6 +1015,21 @@ __global__ void k_clear_words(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// The kernel for K-token groups (K = 1: the one-token schedule); F16H: the
+// fp16-intermediate form.
+template <bool F16H>
+static const void* decode_kernel(int K, bool exact) {
+  if (K == 2) return reinterpret_cast<const void*>(k_decode_groups<2, F16H>);
+  if (K == 4) return reinterpret_cast<const void*>(k_decode_groups<4, F16H>);   // 3, 4 tokens: never exact
+  if (K == 8)
+    return exact ? reinterpret_cast<const void*>(k_decode_groups_any<8, F16H>)
+                 : reinterpret_cast<const void*>(k_decode_groups<8, F16H>);
+  if (K == 16)
+    return exact ? reinterpret_cast<const void*>(k_decode_groups_any<16, F16H>)
+                 : reinterpret_cast<const void*>(k_decode_groups<16, F16H>);
+  return reinterpret_cast<const void*>(k_decode_persistent<F16H>);
+}
+
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   PersistArgs a = args;
   void* kargs[] = {&a};
@@ -1010,17 +1037,10 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   // power of two at or above n: the statically sized kernel leaves K - n
   // groups idle, the exact-range kernel uses every workgroup but runs about
   // a quarter slower per row; measured, the exact ranges win when n < 0.7 K.
-  const void* k = a.interm_mult != 0.f ? reinterpret_cast<const void*>(k_decode_persistent<true>)
-                                       : reinterpret_cast<const void*>(k_decode_persistent<false>);
   const int n = a.n;
   const int K = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
   const bool exact = 10 * n < 7 * K;
-  if (K == 2) k = reinterpret_cast<const void*>(k_decode_groups<2>);
-  else if (K == 4) k = reinterpret_cast<const void*>(k_decode_groups<4>);   // 3, 4 tokens: never exact
-  else if (K == 8) k = exact ? reinterpret_cast<const void*>(k_decode_groups_any<8>)
-                             : reinterpret_cast<const void*>(k_decode_groups<8>);
-  else if (K == 16) k = exact ? reinterpret_cast<const void*>(k_decode_groups_any<16>)
-                              : reinterpret_cast<const void*>(k_decode_groups<16>);
+  const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact) : decode_kernel<false>(K, exact);
   return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
 }
 

@@ -236,9 +236,9 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
   if (((uintptr_t)x | (uintptr_t)out) & 15) return fail(FLINT_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   if (n_tokens < 1 || n_tokens > FLINT_MAX_TOKENS)
     return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_MAX_TOKENS);
-  if (h->interm_div && !(n_tokens == 1 && h->persistent))
-    return fail(FLINT_ERR_UNSUPPORTED, "fp16 intermediates are implemented for single-token calls on the "
-                                       "persistent decode path (n_tokens = %d)", n_tokens);
+  if (h->interm_div && !(n_tokens <= DECODE_MAX_TOKENS && h->persistent))
+    return fail(FLINT_ERR_UNSUPPORTED, "fp16 intermediates are implemented for calls of up to %d tokens on the "
+                                       "persistent decode path (n_tokens = %d)", DECODE_MAX_TOKENS, n_tokens);
   if (layer_begin < 0 || layer_end > h->n_layers || layer_begin >= layer_end)
     return fail(FLINT_ERR_INVALID_ARG, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end,
                 h->n_layers);

@@ -41,9 +41,9 @@ def models():
     m32 = F.FlintMoE(layers)
     del layers
     torch.cuda.empty_cache()
-    ids = torch.full((N_LAYERS, 1, 6), -1, dtype=torch.int32, device="cuda")
-    w = torch.zeros((N_LAYERS, 1, 6), dtype=torch.float32, device="cuda")
-    m16.set_trace(ids, w, 1)
+    ids = torch.full((N_LAYERS, 16, 6), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((N_LAYERS, 16, 6), dtype=torch.float32, device="cuda")
+    m16.set_trace(ids, w, 16)
     yield pack, m16, m32, ids, w
     m16.close()
     m32.close()
@@ -132,7 +132,9 @@ def test_fp16_interm_scaled_layer_needs_the_divisor():
         m.close()
 
 
-def test_fp16_interm_deterministic_and_single_token_only(models):
+def test_fp16_interm_deterministic_and_decode_only(models):
+    """Deterministic; implemented for calls of up to 16 tokens (the prefill
+    path above that returns FLINT_ERR_UNSUPPORTED)."""
     pack, m16, m32, ids, w = models
     x = torch.from_numpy(fg.tokens(0, [990])).cuda()
     a = m16.forward(x)
@@ -141,5 +143,35 @@ def test_fp16_interm_deterministic_and_single_token_only(models):
     m16.status()
     assert torch.equal(a, b)
     with pytest.raises(F.FlintMoEError) as ei:
-        m16.forward(torch.zeros((2, FL.hidden), device="cuda"))
+        m16.forward(torch.zeros((17, FL.hidden), device="cuda"))
     assert ei.value.code == F.FLINT_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 8, 9, 16])
+def test_fp16_interm_token_groups_match_single_tokens(models, n):
+    """Several tokens per call (every group kernel: 2, 4 and 8 and 16 tokens
+    per group size, exact ranges for 5 and 9): each token's output over the
+    three layers is bitwise the one-token call's."""
+    pack, m16, m32, ids, w = models
+    x = torch.from_numpy(fg.tokens(2, range(100, 100 + n))).cuda()
+    together = m16.forward(x)
+    for t in sorted({0, n // 2, n - 1}):
+        alone = m16.forward(x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(alone[0], together[t]), (n, t)
+
+
+def test_fp16_interm_token_group_layer_parity(models):
+    """A four-token call against the oracle's form, teacher-forced per layer
+    and token."""
+    pack, m16, m32, ids, w = models
+    src = SynthSource(pack)
+    cur = fg.tokens(2, range(200, 204))
+    errs = []
+    for l in range(N_LAYERS):
+        nxt = run_forward(m16, cur, l, l + 1)
+        for t in range(4):
+            err, _ = check_layer_fp16(src, l, cur[t], nxt[t], ids[l, t].cpu().numpy(), w[l, t].cpu().numpy())
+            errs.append(err)
+        cur = nxt
+    print(f"fp16 form, 4-token calls vs oracle: rel-L2 max {max(errs):.2e}")
