@@ -249,11 +249,22 @@ __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ id
                                                        const int* __restrict__ offsets, int* __restrict__ perm) {
   const int p = blockIdx.x * PF_NT + threadIdx.x;
   if (p >= n * TOPK) return;
-  const int t = p / TOPK, e = ids[p];
-  const uint32_t* bm = bitmap + e * PF_BW;
+  const int t = p / TOPK, e = ids[p], wt = t >> 5;
+  // the tokens before t in expert e's bitmap: whole words below word wt, all
+  // requested at once (16-byte loads, none waits for another), then the low
+  // bits of word wt
+  const uint4* bm4 = reinterpret_cast<const uint4*>(bitmap + e * PF_BW);
   int pos = offsets[e];
-  for (int i = 0; i < (t >> 5); ++i) pos += __popc(bm[i]);
-  pos += __popc(bm[t >> 5] & ((1u << (t & 31)) - 1u));
+#pragma unroll
+  for (int i = 0; i < PF_BW / 4; ++i) {
+    const uint4 v = bm4[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int word = 4 * i + j;
+      pos += word < wt ? __popc(w[j]) : word == wt ? __popc(w[j] & ((1u << (t & 31)) - 1u)) : 0;
+    }
+  }
   perm[pos] = p;
 }
 
