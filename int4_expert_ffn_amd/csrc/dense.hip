@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(NT, 2) k_rows_mfma(const float* __restrict__ x
 // + 31 of pass p.  h of up to DD_TC tokens is staged in LDS, float4 j of lane
 // chunk (p, L) at (8 p + j) * 64 + L, with the chunk sums beside it.
 constexpr int DD_TC = 4;
-constexpr int DD_ROWS = 4;                    // rows per wave
+constexpr int DD_ROWS = 2;                    // rows per wave
 constexpr int DD_NT = 256;
 constexpr int DD_PMAX = FLINT_DENSE_MLP_SIZE / 2048;
 constexpr int DD_GRID = H / (DD_ROWS * DD_NT / 64);
