@@ -94,7 +94,7 @@ int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* 
 /* Create a handle for weights in the fp16-intermediate pack form (TandemLLM
  * "21 Flint", 21.2: the packs divide each routed expert's up projection by a
  * power of two, expert_interm_div, so that the SwiGLU outputs of the top
- * layers fit fp16, and the engine multiplies the routing weights back).
+ * layers fit fp16; the factor is restored on the routing weights at run time).
  * `weights` as for flint_moe_create, with every routed expert's up-projection
  * scales already divided by interm_div (a power of two in [1, 32768]; 128 in
  * the pages' packs); the shared expert is not divided.  forward on such a

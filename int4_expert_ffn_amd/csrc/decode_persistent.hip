@@ -250,7 +250,7 @@ constexpr int NPOLL = NT - 64;   // polling threads: waves 0 .. NWAVES-2
 
 // F16H: the fp16-intermediate form (TandemLLM "21 Flint", 21.2: packs store
 // each routed expert's up projection divided by a power of two so SwiGLU
-// outputs fit fp16, and the engine multiplies the routing weights back).
+// outputs fit fp16; the divisor goes back in through the routing weights).
 // Every expert's SwiGLU output is rounded to fp16; the h exchange carries two
 // values per word; routed weights are scaled by A.interm_mult in the combine.
 template <bool F16H>

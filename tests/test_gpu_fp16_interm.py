@@ -1,6 +1,6 @@
 """GPU parity of the fp16-intermediate form (TandemLLM "21 Flint", 21.2: packs
 divide each routed expert's up projection by expert_interm_div = 128 so SwiGLU
-outputs fit fp16; the engine multiplies the routing weights back) against the
+outputs fit fp16, and the routing weights carry the factor back) against the
 oracle's form, and its distance from the fp32 path.
 
 Real Flint shape, seeded synthetic weights: the pack form is the same weights

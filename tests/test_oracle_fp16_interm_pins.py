@@ -1,6 +1,6 @@
 """Pins of the oracle's fp16-intermediate form (TandemLLM "21 Flint", 21.2: the
 packs divide each routed expert's up projection by expert_interm_div so SwiGLU
-outputs fit fp16, and the engine multiplies the routing weights back).
+outputs fit fp16, with the factor restored through the routing weights).
 
 The form differs from the fp32 block only by one rounding of each SwiGLU
 output to fp16.  Round to nearest even moves a value v in fp16's normal range
