@@ -11,6 +11,7 @@ Prints one JSON line.  Use --gpus 1 (this build runs on one GPU).
 """
 import argparse
 import hashlib
+import ctypes
 import json
 import os
 import sys
@@ -201,7 +202,7 @@ def bench_prefill(args):
     import flintgen as fg
     import int4_expert_ffn_amd as F
     synth = fg.Synth(fg.FLINT, seed=0, n_layers=1, bias_kind="zipf")
-    model = F.FlintMoE([synth.layer(0, "cuda")])
+    model = _track(F.FlintMoE([synth.layer(0, "cuda")]))
     torch.cuda.empty_cache()
     n = PF_TOKENS
     ids = torch.full((1, n, K), -1, dtype=torch.int32, device="cuda")
@@ -246,6 +247,32 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+_OPEN_MODELS = []
+
+
+def _track(model):
+    """Remember a library handle so that main() closes it before returning:
+    released at interpreter exit instead, its device memory would be freed
+    while the HIP runtime (and a profiler's hooks) are shutting down."""
+    _OPEN_MODELS.append(model)
+    return model
+
+
+def _close_models():
+    """Close the library handles and hand PyTorch's cached device blocks back
+    to the runtime while the process is still running."""
+    import gc
+    import torch
+    if not torch.cuda.is_available():
+        return
+    torch.cuda.synchronize()
+    while _OPEN_MODELS:
+        _OPEN_MODELS.pop().close()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+
+
 def build_stack_model(dev, interm_div=0):
     """The 47-layer stack on ``dev``; interm_div > 0 gives the fp16-intermediate
     pack form of the same weights (routed up scales divided by it)."""
@@ -255,7 +282,7 @@ def build_stack_model(dev, interm_div=0):
     synth = fg.flint_stack(0, N_LAYERS, up_div=interm_div or 1)
     layers = [synth.layer(l, dev) for l in range(N_LAYERS)]
     torch.cuda.synchronize()
-    model = F.FlintMoE(layers, interm_div=interm_div)
+    model = _track(F.FlintMoE(layers, interm_div=interm_div))
     del layers
     torch.cuda.empty_cache()
     return model
@@ -588,41 +615,171 @@ def cpu_baseline_head(seconds_budget=20.0):
             "sample": f"one token, head rows 0..{rows - 1} in blocks of 4,096 ({spent:.1f} s of oracle time)"}
 
 
+class _CachedLayers:
+    """Oracle source over tensors generated before the clock starts: the
+    router, bias, shared expert and the experts a token selects, per layer."""
+
+    def __init__(self, synth, picks):
+        self.router_ = {l: synth.router(l).numpy() for l in picks}
+        self.bias_ = {l: synth.bias(l).numpy() for l in picks}
+        self.shared_ = {l: {k: v.numpy() for k, v in synth.shared(l).items()} for l in picks}
+        self.ex_ = {l: (list(ids), {k: v.numpy() for k, v in synth.experts(l, list(ids)).items()})
+                    for l, ids in picks.items()}
+
+    def router(self, l):
+        return self.router_[l]
+
+    def bias(self, l):
+        return self.bias_[l]
+
+    def shared(self, l):
+        return self.shared_[l]
+
+    def experts(self, l, ids):
+        have, d = self.ex_[l]
+        idx = [have.index(int(e)) for e in ids]
+        return {k: v[idx] for k, v in d.items()}
+
+
 def cpu_baseline(seconds_budget=20.0, interm_div=0):
-    """The CPU oracle (fp64 NumPy) on a bounded sample: one token through as
-    many of the 47 layers as fit the budget; scaled to tokens/s for the whole
-    stack.  interm_div > 0: the oracle's fp16-intermediate form on the pack
-    weights."""
+    """The CPU oracle (fp64 NumPy, explicit dequantisation, full sort) timed
+    alone: one token through the 47-layer stack, with every tensor the token
+    touches generated before the clock starts (a first, untimed pass finds
+    the experts it selects).  Reported: tokens/s through the 47 layers with
+    the BLAS library's threads, the one-layer rate (the single-layer
+    workload), and the same with one thread.  Each timed pass stops early
+    past its share of the budget and is scaled to the 47 layers.
+    interm_div > 0: the oracle's fp16-intermediate form on the pack weights."""
     import flintgen as fg
     from oracle import flint_oracle as O
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from oracle_sources import SynthSource
+    import threadpoolctl
     synth = fg.flint_stack(0, N_LAYERS, up_div=interm_div or 1)
-    src = SynthSource(synth)
-    x = fg.token(0, 0)
-    t0 = time.perf_counter()
-    layers = 0
+
+    def block(a, src, l):
+        return (O.moe_block_fp16_interm(a, src, l, fg.FLINT, interm_div) if interm_div
+                else O.moe_block(a, src, l, fg.FLINT))
+
+    class _Lazy:   # the untimed pass: generates on demand, records the picks
+        def __init__(self):
+            self.picks = {}
+
+        def router(self, l):
+            return synth.router(l).numpy()
+
+        def bias(self, l):
+            return synth.bias(l).numpy()
+
+        def shared(self, l):
+            return {k: v.numpy() for k, v in synth.shared(l).items()}
+
+        def experts(self, l, ids):
+            self.picks[l] = [int(e) for e in ids]
+            return {k: v.numpy() for k, v in synth.experts(l, ids).items()}
+
+    x0 = fg.token(0, 0)
+    lazy = _Lazy()
+    x = x0
     for l in range(N_LAYERS):
-        a = O.block_input(x, fg.FLINT)
-        res = (O.moe_block_fp16_interm(a, src, l, fg.FLINT, interm_div) if interm_div
-               else O.moe_block(a, src, l, fg.FLINT))
-        x = (x.astype(np.float64) + res.delta).astype(np.float32)
-        layers += 1
-        if time.perf_counter() - t0 > seconds_budget:
-            break
-    dt = time.perf_counter() - t0
-    per_token = dt / layers * N_LAYERS
-    try:
-        import threadpoolctl
-        cores = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        cores = 1
-    return {"value": round(1.0 / per_token, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 token through layers 0..{layers - 1} of the 47-layer stack ({dt:.1f} s, "
-                      f"weights regenerated per layer included), scaled to 47 layers"}
+        x = (x.astype(np.float64) + block(O.block_input(x, fg.FLINT), lazy, l).delta).astype(np.float32)
+    src = _CachedLayers(synth, lazy.picks)
+
+    def timed(budget):
+        x, per_layer = x0, []
+        t_start = time.perf_counter()
+        for l in range(N_LAYERS):
+            t0 = time.perf_counter()
+            res = block(O.block_input(x, fg.FLINT), src, l)
+            per_layer.append(time.perf_counter() - t0)
+            x = (x.astype(np.float64) + res.delta).astype(np.float32)
+            if time.perf_counter() - t_start > budget:
+                break
+        return per_layer
+
+    threads = _oracle_threads()
+    all_t = timed(seconds_budget * 0.6)
+    with threadpoolctl.threadpool_limits(1):
+        one_t = timed(seconds_budget * 0.4)
+    per_token = float(np.mean(all_t)) * N_LAYERS
+    per_token_1 = float(np.mean(one_t)) * N_LAYERS
+    return {"value": round(1.0 / per_token, 6), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 token through layers 0..{len(all_t) - 1} of the 47-layer stack, oracle calls only "
+                      f"(tensors generated before timing), scaled to 47 layers",
+            "cpu_count": os.cpu_count(),
+            "one_layer_tokens_per_s": round(1.0 / float(np.mean(all_t)), 4),
+            "one_thread_tokens_per_s": round(1.0 / per_token_1, 6),
+            "one_thread_sample_layers": len(one_t)}
+
+
+# Phase markers of the decode kernel's profiling build (thread 0 of each
+# workgroup records the wall clock at marker k of layer l): the phases are the
+# intervals between consecutive markers of one workgroup.
+PHASES = (("x gather", 0, 1), ("norm (block input)", 1, 2), ("router (and the shared rows' wait)", 2, 4),
+          ("(c, s) gather", 4, 5), ("routing (top-6, weights)", 5, 7), ("gate/up", 7, 8),
+          ("h gather", 8, 9), ("down and combine", 9, 10))
+
+
+def bench_phase_table(args):
+    """Phase durations of the single-token decode kernel (profiling build
+    libflint_moe_phase.so): median over workgroups and over layers 1..46 of
+    10 calls of the bench workload (47 layers, 1 token)."""
+    import torch
+    import flintgen as fg
+    import int4_expert_ffn_amd as F
+    F.LIB_PATH = os.path.join(F.HERE, "libflint_moe_phase.so")
+    if not os.path.exists(F.LIB_PATH):
+        raise FileNotFoundError(f"{F.LIB_PATH} is missing: python -m int4_expert_ffn_amd.build --phase-ts")
+    L = F.lib()
+    L.flint_moe_debug_phase_ts.argtypes = [ctypes.c_void_p]
+    L.flint_moe_debug_phase_ts.restype = ctypes.c_int
+    dev = torch.device("cuda", 0)
+    model = build_stack_model(dev, args.interm_div)
+    pool = torch.from_numpy(fg.tokens(0, range(64))).to(dev)
+    out = torch.empty((1, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    nl, nm, nwg = 48, 16, 256
+    buf = np.zeros((nl, nm, nwg), dtype=np.uint64)
+    for i in range(args.warmup):
+        F.flint_moe_forward(model.h, pool[i % 64:i % 64 + 1], 1, 0, N_LAYERS, out, stream)
+    torch.cuda.synchronize()
+    per_phase = [[] for _ in PHASES]
+    layer_us = []
+    for i in range(10):
+        F.flint_moe_forward(model.h, pool[i % 64:i % 64 + 1], 1, 0, N_LAYERS, out, stream)
+        torch.cuda.synchronize()
+        rc = L.flint_moe_debug_phase_ts(buf.ctypes.data)
+        assert rc == 0, rc
+        ts = buf.astype(np.float64) * 0.01   # 100 MHz ticks -> us
+        for l in range(1, N_LAYERS):
+            for p, (_, a, b) in enumerate(PHASES):
+                per_phase[p].extend((ts[l][b] - ts[l][a]).tolist())
+            layer_us.extend((ts[l][10] - ts[l - 1][10]).tolist())
+    model.status()
+    if args.phase_raw_out:   # raw per-workgroup timestamps of the last call, for inspection
+        np.save(args.phase_raw_out, buf)
+    lines = ["# decode phase table: 47-layer stack, 1 token; per-workgroup phase durations, median over"
+             " the 256 workgroups and layers 1..46 of 10 calls",
+             "# command: python -m int4_expert_ffn_amd.build --phase-ts && python bench.py --phase-table"
+             + (f" --interm-div {args.interm_div}" if args.interm_div else ""),
+             f"# kernel_sources_sha16: {kernel_source_hash('decode')}",
+             f"# layer time (marker to marker): {np.median(layer_us):.2f} us",
+             "phase, us"]
+    for p, (name, _, _) in enumerate(PHASES):
+        lines.append(f"{name:40s} {np.median(per_phase[p]):7.2f}")
+    text = "\n".join(lines)
+    print(text, flush=True)
+    if args.phase_table_out:
+        with open(args.phase_table_out, "w") as f:
+            f.write(text + "\n")
 
 
 def main():
+    try:
+        return _main()
+    finally:
+        _close_models()
+
+
+def _main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -647,6 +804,10 @@ def main():
                     help="time the decode attention with sinks instead (full layer at 100,000 positions, window layer)")
     ap.add_argument("--attn-batch1", action="store_true",
                     help="with --attn: only the batch-1 full layer (for a kernel trace of that one shape)")
+    ap.add_argument("--phase-table", action="store_true",
+                    help="decode phase timestamps (needs the --phase-ts build of the library)")
+    ap.add_argument("--phase-table-out", default=None, help="write the phase table to this file")
+    ap.add_argument("--phase-raw-out", default=None, help="save the raw timestamps of the last call (.npy)")
     ap.add_argument("--interm-div", type=int, default=0,
                     help="time the fp16-intermediate form instead: the same stack with routed up projections "
                          "divided by this power of two (128 in the published packs)")
@@ -654,6 +815,8 @@ def main():
     if args.counters_summary:
         summarize_counters(*args.counters_summary, commands=args.command, which=args.counters_kernel)
         return
+    if args.phase_table:
+        return bench_phase_table(args)
     if args.prefill:
         bench_prefill(args)
         return

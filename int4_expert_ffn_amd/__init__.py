@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libflint_moe.so")
+# FLINT_MOE_LIBRARY selects another build of the same library (the profiling
+# build with phase timestamps); by default the in-tree libflint_moe.so.
+LIB_PATH = os.environ.get("FLINT_MOE_LIBRARY") or os.path.join(HERE, "libflint_moe.so")
 
 FLINT_HIDDEN = 2048
 FLINT_EXPERTS = 256

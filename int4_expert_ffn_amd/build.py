@@ -1,4 +1,10 @@
-"""Build libflint_moe.so (all HIP sources of csrc/) for gfx950 with hipcc, in-tree."""
+"""Build libflint_moe.so (all HIP sources of csrc/) for gfx950 with hipcc, in-tree.
+
+``python -m int4_expert_ffn_amd.build --phase-ts`` builds the profiling
+variant libflint_moe_phase.so instead: the decode kernel then records the wall
+clock at each phase of the first 16 layers of a call (flint_moe_debug_phase_ts),
+read by ``bench.py --phase-table`` (set FLINT_MOE_LIBRARY to that file).
+"""
 import glob
 import os
 import subprocess
@@ -6,16 +12,18 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libflint_moe.so")
+LIB_PHASE = os.path.join(HERE, "libflint_moe_phase.so")
 ARCH = "gfx950"
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, phase_ts: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    lib = LIB_PHASE if phase_ts else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(HERE, "..", "include"), "-o", tmp] + srcs
+           "-I", os.path.join(HERE, "..", "include"), "-o", tmp] + (["-DFLINT_PHASE_TS"] if phase_ts else []) + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -24,9 +32,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg:
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, phase_ts="--phase-ts" in sys.argv[1:]))
