@@ -70,6 +70,28 @@ int flint_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int 
                       const int32_t* pos, int n_tokens, int window, float* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Size of the library's own scratch for flint_attn_decode_noalloc: 16 MiB of
+ * device memory per GPU, held from the first such call on that GPU until the
+ * process ends. */
+#define FLINT_ATT_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* flint_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  The chunk partials go to
+ * a fixed scratch array of FLINT_ATT_SCRATCH_BYTES that the library holds per
+ * GPU; the call itself allocates nothing (its first call on a GPU looks up the
+ * array's device address).  The same arguments, rules and results as
+ * flint_attn_decode, bitwise; in addition flint_attn_workspace_bytes(n_tokens,
+ * max_seen) must not exceed FLINT_ATT_SCRATCH_BYTES (FLINT_ERR_INVALID_ARG
+ * otherwise: for one token, up to 253,952 visible positions; for 16 tokens,
+ * up to 15,872 each).  Every call on one GPU uses that GPU's one scratch
+ * array: calls that may run at the same time on one GPU (on different
+ * streams, or from different threads) race and must be serialised by the
+ * caller. */
+int flint_attn_decode_noalloc(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows,
+                              const float* sinks, const int32_t* pos, int n_tokens, int window, float* out,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

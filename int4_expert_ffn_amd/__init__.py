@@ -41,10 +41,11 @@ FLINT_ATT_HEAD_DIM = 128
 FLINT_ATT_WINDOW = 513
 FLINT_ATT_RING = 640
 FLINT_ATT_MAX_TOKENS = 16
+FLINT_ATT_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ("flint_moe_create", "flint_moe_create_fp16_interm", "flint_moe_forward", "flint_moe_set_trace",
             "flint_moe_status", "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward",
-            "flint_head_forward", "flint_attn_workspace_bytes", "flint_attn_decode")
+            "flint_head_forward", "flint_attn_workspace_bytes", "flint_attn_decode", "flint_attn_decode_noalloc")
 
 
 class flint_q4(ctypes.Structure):
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.flint_attn_decode.argtypes = [vp, vp, vp, ci, vp, ctypes.POINTER(ctypes.c_int32), ci, ci, vp, vp,
                                         ctypes.c_size_t, vp]
         L.flint_attn_decode.restype = ci
+        L.flint_attn_decode_noalloc.argtypes = [vp, vp, vp, ci, vp, ctypes.POINTER(ctypes.c_int32), ci, ci, vp, vp]
+        L.flint_attn_decode_noalloc.restype = ci
         _lib = L
     return _lib
 
@@ -190,6 +193,13 @@ def flint_attn_decode(q, k, v, ring_rows, sinks, pos, n_tokens, window, out, wor
     p = (ctypes.c_int32 * n_tokens)(*[int(x) for x in pos])
     _check(lib().flint_attn_decode(_ptr(q), _ptr(k), _ptr(v), ring_rows, _ptr(sinks), p, n_tokens, window, _ptr(out),
                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def flint_attn_decode_noalloc(q, k, v, ring_rows, sinks, pos, n_tokens, window, out, stream=None) -> None:
+    """flint_attn_decode with the library's fixed scratch instead of a workspace."""
+    p = (ctypes.c_int32 * n_tokens)(*[int(x) for x in pos])
+    _check(lib().flint_attn_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), ring_rows, _ptr(sinks), p, n_tokens, window,
+                                           _ptr(out), _stream(stream)))
 
 
 def _stream(stream):

@@ -18,6 +18,8 @@
 // Each token's chunks are computed the same way whatever the other tokens
 // are, and every sum has a fixed order, so results are deterministic and
 // bitwise independent of the token count.
+#include <mutex>
+
 #include "attn.h"
 
 namespace flint {
@@ -342,6 +344,35 @@ __global__ void __launch_bounds__(ACD * ACS) k_attn_combine(const float* __restr
     }
     out[((size_t)t * AQ + h) * AD + d] = At / Lt;
   }
+}
+
+// Scratch of the allocation-free entry point (flint_attn_decode_noalloc): the
+// chunk partials live in this file-scope device array, which every GPU the
+// library runs on holds until the process ends.  In host code `scratch` only
+// names the symbol; its device address, per device, comes from
+// hipGetSymbolAddress on the first call on that device (attn_scratch).  Each
+// call writes every partial it reads, so nothing needs clearing between calls.
+__device__ __align__(256) float scratch[ATTN_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_dev[ATTN_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t attn_scratch(float** p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= ATTN_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<float*>(a);
+  }
+  *p = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 size_t attn_workspace_bytes(int n_tokens, int max_seen) {

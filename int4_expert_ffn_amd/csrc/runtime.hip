@@ -389,18 +389,20 @@ size_t flint_attn_workspace_bytes(int n_tokens, int max_seen) {
   return attn_workspace_bytes(n_tokens, max_seen);
 }
 
-int flint_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows, const float* sinks,
-                      const int32_t* pos, int n_tokens, int window, float* out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !sinks || !pos || !out || !workspace)
-    return fail(FLINT_ERR_INVALID_ARG, "q, k, v, sinks, pos, out or workspace is NULL");
-  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(workspace))
-    return fail(FLINT_ERR_INVALID_ARG, "q, k, v, out and workspace must be 16-byte aligned");
+// Checks shared by the two attention entry points: the visible range of every
+// token (first[t], count[t]) and the most positions any token sees.
+static int attn_check(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows, const float* sinks,
+                      const int32_t* pos, int n_tokens, int window, float* out, int* first, int* count,
+                      int* max_seen) {
+  if (!q || !k || !v || !sinks || !pos || !out)
+    return fail(FLINT_ERR_INVALID_ARG, "q, k, v, sinks, pos or out is NULL");
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out))
+    return fail(FLINT_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (n_tokens < 1 || n_tokens > FLINT_ATT_MAX_TOKENS)
     return fail(FLINT_ERR_INVALID_ARG, "n_tokens = %d outside [1, %d]", n_tokens, FLINT_ATT_MAX_TOKENS);
   if (ring_rows < 1) return fail(FLINT_ERR_INVALID_ARG, "ring_rows = %d must be positive", ring_rows);
   if (window < 0) return fail(FLINT_ERR_INVALID_ARG, "window = %d must not be negative", window);
-  int first[FLINT_ATT_MAX_TOKENS], count[FLINT_ATT_MAX_TOKENS], max_seen = 0;
+  *max_seen = 0;
   for (int t = 0; t < n_tokens; ++t) {
     if (pos[t] < 0) return fail(FLINT_ERR_INVALID_ARG, "pos[%d] = %d is negative", t, pos[t]);
     first[t] = window ? std::max(0, pos[t] - window + 1) : 0;
@@ -408,17 +410,48 @@ int flint_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int 
     if (count[t] > ring_rows)
       return fail(FLINT_ERR_INVALID_ARG, "token %d sees %d positions, more than the %d cache rows", t, count[t],
                   ring_rows);
-    max_seen = std::max(max_seen, count[t]);
+    *max_seen = std::max(*max_seen, count[t]);
   }
+  const size_t qb = (size_t)n_tokens * FLINT_ATT_Q_HEADS * FLINT_ATT_HEAD_DIM * sizeof(float);
+  if (overlap(q, qb, out, qb)) return fail(FLINT_ERR_INVALID_ARG, "out overlaps q");
+  return FLINT_OK;
+}
+
+int flint_attn_decode(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows, const float* sinks,
+                      const int32_t* pos, int n_tokens, int window, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int first[FLINT_ATT_MAX_TOKENS], count[FLINT_ATT_MAX_TOKENS], max_seen = 0;
+  int rc = attn_check(q, k, v, ring_rows, sinks, pos, n_tokens, window, out, first, count, &max_seen);
+  if (rc) return rc;
+  if (!workspace) return fail(FLINT_ERR_INVALID_ARG, "workspace is NULL");
+  if (misaligned16(workspace)) return fail(FLINT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const size_t need = attn_workspace_bytes(n_tokens, max_seen);
   if (workspace_bytes < need)
     return fail(FLINT_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   const size_t qb = (size_t)n_tokens * FLINT_ATT_Q_HEADS * FLINT_ATT_HEAD_DIM * sizeof(float);
-  if (overlap(q, qb, out, qb)) return fail(FLINT_ERR_INVALID_ARG, "out overlaps q");
   if (overlap(workspace, need, out, qb) || overlap(workspace, need, q, qb))
     return fail(FLINT_ERR_INVALID_ARG, "workspace overlaps q or out");
   const hipError_t e = launch_attn_decode(q, k, v, ring_rows, sinks, first, count, n_tokens, out, (float*)workspace,
                                           (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "attention launch");
+  return FLINT_OK;
+}
+
+int flint_attn_decode_noalloc(const float* q, const uint16_t* k, const uint16_t* v, int ring_rows,
+                              const float* sinks, const int32_t* pos, int n_tokens, int window, float* out,
+                              void* stream) {
+  int first[FLINT_ATT_MAX_TOKENS], count[FLINT_ATT_MAX_TOKENS], max_seen = 0;
+  int rc = attn_check(q, k, v, ring_rows, sinks, pos, n_tokens, window, out, first, count, &max_seen);
+  if (rc) return rc;
+  const size_t need = attn_workspace_bytes(n_tokens, max_seen);
+  if (need > ATTN_SCRATCH_BYTES)
+    return fail(FLINT_ERR_INVALID_ARG,
+                "%d tokens seeing up to %d positions need %zu bytes of scratch, above the %zu this entry point holds",
+                n_tokens, max_seen, need, ATTN_SCRATCH_BYTES);
+  float* ws = nullptr;
+  hipError_t e = attn_scratch(&ws);
+  if (e != hipSuccess) return fail_hip(e, "attention scratch address");
+  e = launch_attn_decode(q, k, v, ring_rows, sinks, first, count, n_tokens, out, ws, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "attention launch");
   return FLINT_OK;
 }

@@ -77,6 +77,21 @@ def test_attention_rejects_bad_arguments_before_any_hip_call():
     assert call([10], out=A) == inval                      # out overlaps q
     assert "overlaps" in F.flint_moe_last_error()
     assert lib.flint_attn_decode(None, A, A, 640, A, (ctypes.c_int32 * 1)(3), 1, 513, A, A, ws, None) == inval
+    # the allocation-free variant: the same checks, and its scratch limit
+    def call_na(pos, n=None, window=513, ring=640, q=A, out=1 << 20):
+        n = len(pos) if n is None else n
+        p = (ctypes.c_int32 * max(1, len(pos)))(*pos)
+        return lib.flint_attn_decode_noalloc(q, A, A, ring, A, p, n, window, out, None)
+
+    assert call_na([10], n=0) == inval
+    assert call_na([-1]) == inval
+    assert call_na([700], window=0) == inval
+    assert call_na([10], out=A) == inval
+    assert call_na([15872] * 16, window=0, ring=16000) == inval   # 16 x 63 chunks: above the 16 MiB scratch
+    assert "scratch" in F.flint_moe_last_error()
+    assert call_na([253952], window=0, ring=300000) == inval       # one token, 993 chunks
+    assert F.flint_attn_workspace_bytes(1, 253952) <= F.FLINT_ATT_SCRATCH_BYTES
+    assert F.flint_attn_workspace_bytes(16, 15872) <= F.FLINT_ATT_SCRATCH_BYTES
 
 
 def test_create_rejects_bad_arguments_before_any_hip_call():
