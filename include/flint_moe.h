@@ -70,7 +70,7 @@ typedef struct {
   const uint16_t* scales;
 } flint_q4;
 
-/* One MoE layer, all device pointers (16-byte aligned).
+/* One MoE layer, all device pointers (any alignment: create copies them).
  *   router_w    [E][H]   bf16 bits
  *   router_bias [E]      fp32
  *   gate, up    [E][I][H/2] codes,  [E][I][H/G] scales
@@ -136,6 +136,15 @@ int flint_moe_set_trace(flint_moe_t h, int32_t* ids, float* weights, int capacit
 /* Blocking: wait for the handle's work on `stream` and report FLINT_ERR_DEVICE
  * if a device-side check fired (for example a bounded wait that expired). */
 int flint_moe_status(flint_moe_t h, void* stream);
+
+/* Testing hook.  Decode calls tag the words they exchange between workgroups
+ * with a per-call counter that advances by 256 each call; when it would wrap,
+ * the call clears the exchange buffers first and restarts the counter.  This
+ * sets the counter so that a test reaches that branch in a few calls.
+ * `epoch` must be a multiple of 256 and not below the current value (a lower
+ * one could match tags left by earlier calls): FLINT_ERR_INVALID_ARG
+ * otherwise.  Not thread-safe with respect to calls on the same handle. */
+int flint_moe_debug_set_epoch(flint_moe_t h, uint32_t epoch);
 
 /* Release the handle and its device memory.  NULL is ignored. */
 void flint_moe_destroy(flint_moe_t h);

@@ -329,6 +329,14 @@ int flint_moe_status(flint_moe_t h, void* stream) {
   return FLINT_OK;
 }
 
+int flint_moe_debug_set_epoch(flint_moe_t h, uint32_t epoch) {
+  if (!h) return fail(FLINT_ERR_INVALID_ARG, "handle is NULL");
+  if (epoch & 255u) return fail(FLINT_ERR_INVALID_ARG, "epoch %u is not a multiple of 256", epoch);
+  if (epoch < h->epoch) return fail(FLINT_ERR_INVALID_ARG, "epoch %u is below the current %u", epoch, h->epoch);
+  h->epoch = epoch;
+  return FLINT_OK;
+}
+
 void flint_moe_destroy(flint_moe_t h) { release(h); }
 
 // ------------------------------------------------------------- dense MLP and head

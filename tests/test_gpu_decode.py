@@ -233,3 +233,27 @@ def test_writes_stay_inside_out(model):
         torch.cuda.synchronize()
         assert bool((out[n * FL.hidden:] == sentinel).all()), n
         assert torch.equal(out[: n * FL.hidden].view(torch.float32).view(n, FL.hidden), ref), n
+
+
+def test_exchange_tag_wrap_clears_buffers_and_keeps_results(model):
+    """Decode calls tag exchanged words with a per-call counter; where it would
+    wrap, the call clears the exchange buffers and restarts it.  With the
+    counter set just below the wrap, single-token and four-token calls before,
+    across and after it give the results of ordinary calls, bitwise."""
+    synth, m, ids, w = model
+    x = torch.from_numpy(fg.tokens(0, range(900, 904))).cuda()
+    ref1 = m.forward(x[:1])
+    ref4 = m.forward(x)
+    torch.cuda.synchronize()
+    with pytest.raises(F.FlintMoEError):
+        m.debug_set_epoch(0xFFFFFB80)          # not a multiple of 256
+    with pytest.raises(F.FlintMoEError):
+        m.debug_set_epoch(256)                 # below the current counter
+    m.debug_set_epoch(0xFFFFFB00)
+    outs = []
+    for i in range(6):                         # counter: ..FC00, ..FD00, ..FE00, wrap -> 256, 512, 768
+        outs.append((m.forward(x[:1]) if i % 2 == 0 else m.forward(x), i % 2))
+    torch.cuda.synchronize()
+    m.status()
+    for i, (o, kind) in enumerate(outs):
+        assert torch.equal(o, ref4 if kind else ref1), i
