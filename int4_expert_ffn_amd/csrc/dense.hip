@@ -43,97 +43,6 @@ __device__ __forceinline__ void expand8(uint32_t code, uint32_t* p) {
   p[3] = __builtin_amdgcn_perm(K43, hi, 0x04030402u);
 }
 
-// Lane part of one K = 2048 row for one token from expanded codes: the 32
-// products summed in fp32 in a fixed order, minus 136 * (sum of the lane's
-// activations), times the row's scale.
-__device__ __forceinline__ float lane_dot_expanded(const uint32_t (&p)[16], const uint4 (&a)[4], float asum,
-                                                   float scale) {
-  float acc = 0.f;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t av[4] = {a[d].x, a[d].y, a[d].z, a[d].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p[4 * d + q]),
-                                            __builtin_bit_cast(bf16x2_t, av[q]), acc, false);
-  }
-  return fmaf(-136.f, asum, acc) * scale;
-}
-
-// Wave w of the grid takes rows w, w + waves, ...; U rows per batch and three
-// batches in a ring, two in flight while one is used (loads are never
-// conditional, so waiting for one batch never waits for a younger one: rows
-// past the wave's last one re-read it).  The first two batches are requested
-// before the block inputs are computed.  Each row's codes are expanded once
-// and used for every token.
-// SWIGLU: y[t][r] = silu(W0[r] . a_t) * (W1[r] . a_t), else y[t][r] = W0[r] . a_t.
-template <bool SWIGLU, int U>
-__global__ void __launch_bounds__(NT, 2) k_rows_k2048(const float* __restrict__ x, int n,
-                                                      const uint8_t* __restrict__ c0, const uint16_t* __restrict__ s0,
-                                                      const uint8_t* __restrict__ c1, const uint16_t* __restrict__ s1,
-                                                      int rows, float* __restrict__ y) {
-  __shared__ DenseInput in;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gw = blockIdx.x * NWAVES + wave, nw = gridDim.x * NWAVES;
-  const int my_rows = gw < rows ? (rows - 1 - gw) / nw + 1 : 1;   // waves past the last row re-read row 0..
-  const int nb = gw < rows ? (my_rows + U - 1) / U : 0;
-  auto row_of = [&](int j) { return (size_t)min(gw, rows - 1) + (size_t)min(j, my_rows - 1) * nw; };
-  auto load = [&](int b, uint4 (&c)[U], uint32_t (&sc)[U], uint4 (&cu)[U], uint32_t (&su)[U]) {
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const size_t r = row_of(b * U + i);
-      c[i] = reinterpret_cast<const uint4*>(c0 + r * (H / 2))[lane];
-      sc[i] = s0[r * (H / G) + (lane >> 2)];
-      if (SWIGLU) {
-        cu[i] = reinterpret_cast<const uint4*>(c1 + r * (H / 2))[lane];
-        su[i] = s1[r * (H / G) + (lane >> 2)];
-      }
-    }
-  };
-  auto compute = [&](int b, const uint4 (&c)[U], const uint32_t (&sc)[U], const uint4 (&cu)[U],
-                     const uint32_t (&su)[U]) {
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-      const int j = b * U + i;
-      if (j >= my_rows) break;   // wave-uniform
-      const size_t r = row_of(j);
-      uint32_t pg[16], pu[16];
-      expand8(c[i].x, pg);
-      expand8(c[i].y, pg + 4);
-      expand8(c[i].z, pg + 8);
-      expand8(c[i].w, pg + 12);
-      if (SWIGLU) {
-        expand8(cu[i].x, pu);
-        expand8(cu[i].y, pu + 4);
-        expand8(cu[i].z, pu + 8);
-        expand8(cu[i].w, pu + 12);
-      }
-      const float sg = bf16_bits_to_f32(sc[i]), su_f = SWIGLU ? bf16_bits_to_f32(su[i]) : 0.f;
-      for (int t = 0; t < n; ++t) {
-        const uint4* at = reinterpret_cast<const uint4*>(in.a[t]);
-        const uint4 av[4] = {at[lane], at[64 + lane], at[128 + lane], at[192 + lane]};
-        const float asum = in.asum[t][lane];
-        float v = wave_sum(lane_dot_expanded(pg, av, asum, sg));
-        if (SWIGLU) v = silu_mul(v, wave_sum(lane_dot_expanded(pu, av, asum, su_f)));
-        if (lane == 0) y[(size_t)t * rows + r] = v;
-      }
-    }
-  };
-  uint4 ca[U], cb[U], cc[U], ua[U], ub[U], uc[U];
-  uint32_t sa[U], sb[U], sc_[U], ta[U], tb[U], tc[U];
-  load(0, ca, sa, ua, ta);
-  load(1, cb, sb, ub, tb);
-  dense_inputs(x, n, in);   // the only barrier; every wave gets here
-  for (int b = 0; b < nb; b += 3) {
-    load(b + 2, cc, sc_, uc, tc);
-    compute(b, ca, sa, ua, ta);
-    load(b + 3, ca, sa, ua, ta);
-    compute(b + 1, cb, sb, ub, tb);
-    load(b + 4, cb, sb, ub, tb);
-    compute(b + 2, cc, sc_, uc, tc);
-  }
-}
-
 typedef __bf16 dn_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float dn_f32x4 __attribute__((ext_vector_type(4)));
 
@@ -169,8 +78,6 @@ struct DenseTokens {
 // bf16 parts (exact products).  A block streams as two chunks of 8 K-groups,
 // the next chunk in flight while one is used.
 // SWIGLU: y[t][r] = silu(W0[r] . a_t) * (W1[r] . a_t), else y[t][r] = W0[r] . a_t.
-// The head runs here; the dense MLP's gate/up run in k_rows_k2048 (6,144 rows
-// make only 384 blocks of 16, too few to fill the chip).
 template <bool SWIGLU>
 __global__ void __launch_bounds__(NT, 2) k_rows_mfma(const float* __restrict__ x, int n,
                                                      const uint8_t* __restrict__ c0, const uint16_t* __restrict__ s0,
@@ -287,84 +194,378 @@ __global__ void __launch_bounds__(NT, 2) k_rows_mfma(const float* __restrict__ x
   }
 }
 
-// ------------------------------------------------------------- dense down
-// out[t][c] = x[t][c] + Wd[c] . h_t, K = inter = P x 2048.  Wave w of
-// workgroup b owns rows 16 b + 4 w .. + 3; lane L covers k = 2048 p + 32 L ..
-// + 31 of pass p.  h of up to DD_TC tokens is staged in LDS, float4 j of lane
-// chunk (p, L) at (8 p + j) * 64 + L, with the chunk sums beside it.
-constexpr int DD_TC = 4;
-constexpr int DD_ROWS = 2;                    // rows per wave
-constexpr int DD_NT = 256;
-constexpr int DD_PMAX = FLINT_DENSE_MLP_SIZE / 2048;
-constexpr int DD_GRID = H / (DD_ROWS * DD_NT / 64);
+// ------------------------------------------------------------- dense MLP
+// Both products of the dense MLP run on the matrix cores with the call's
+// tokens as the M dimension of v_mfma_f32_16x16x32_bf16 (zeros past n) and 16
+// weight rows as N, so a token's arithmetic never depends on the other tokens.
+// The codes become bf16 16 + n' = code + 24 (n' = code + 8 in [0, 15]: low
+// byte 0x80 | n' << 3 under the high byte 0x41), in the pair order of the
+// activations; each K-group's products sum (code + 24) v over its 128 elements
+// exactly, are scaled by the row's scale, and 24 s R is removed, R the group's
+// sum of v.  (The smaller offset of 24, against 136 in the head, keeps the
+// cancellation at the down projection's 6,144-element rows small.)
+__device__ __forceinline__ uint4 expand8_o24(uint32_t code) {
+  const uint32_t x = code ^ 0x88888888u;
+  const uint32_t lo = ((x & 0x0F0F0F0Fu) << 3) | 0x80808080u;   // bytes: k0, k2, k4, k6
+  const uint32_t hi = ((x >> 1) & 0x78787878u) | 0x80808080u;   // bytes: k1, k3, k5, k7
+  const uint32_t K41 = 0x41414141u;
+  return make_uint4(__builtin_amdgcn_perm(K41, lo, 0x04010400u), __builtin_amdgcn_perm(K41, lo, 0x04030402u),
+                    __builtin_amdgcn_perm(K41, hi, 0x04010400u), __builtin_amdgcn_perm(K41, hi, 0x04030402u));
+}
 
-__global__ void __launch_bounds__(DD_NT) k_dense_down(const float* __restrict__ h, int n, int inter,
-                                                      const uint8_t* __restrict__ dc, const uint16_t* __restrict__ ds,
-                                                      const float* x, float* out) {
-  __shared__ float4 hb[DD_TC][FLINT_DENSE_MLP_SIZE / 4];
-  __shared__ float hsum[DD_TC][DD_PMAX * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int P = inter / 2048, q4 = inter / 4;
-  const int r0 = (blockIdx.x * (DD_NT / 64) + wave) * DD_ROWS;
-  uint4 code[DD_ROWS][DD_PMAX];
-  uint32_t sc[DD_ROWS][DD_PMAX];
+// Pair order of 8 bf16 values v0..v7: (v0,v2), (v4,v6), (v1,v3), (v5,v7).
+__device__ __forceinline__ uint4 pack_pair_order(const uint32_t (&b)[8]) {
+  return make_uint4(b[0] | (b[2] << 16), b[4] | (b[6] << 16), b[1] | (b[3] << 16), b[5] | (b[7] << 16));
+}
+
+// Block input of token t by one wave.  Lane L holds the 8-element chunks
+// L + 64 j (j < 4), elements 8 (L + 64 j) .. + 7, as float4s 2 j and 2 j + 1
+// of xv (xt is the token's row, re-read on the rare exact path).  RMSNorm in
+// fp64 (exact squares, a per-lane sum in order, then the fixed wave tree), one
+// rounding to bf16.  Writes the chunks as MFMA operands at[t][c] (consecutive
+// lanes on consecutive 16-byte slots) and, per K-group g (chunks 16 g .. 16 g
+// + 15: lanes 16 (g % 4) .. + 15 of chunk set j = g / 4), the sum of its 128
+// bf16 values to R[t][g].
+constexpr int DG_ROW = H / 8 + 1;   // LDS row of one token's chunks, padded so rows start on other banks
+
+__device__ __forceinline__ void wave_block_input_store(const uint32_t (&b)[32], int t, uint4 (*at)[DG_ROW],
+                                                       float (*R)[H / G]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < DD_ROWS; ++i)
+  for (int j = 0; j < 4; ++j) {
+    uint32_t cb[8];
+    float part = 0.f;
 #pragma unroll
-    for (int p = 0; p < DD_PMAX; ++p) {
-      const int pp = p < P ? p : 0;
-      code[i][p] = reinterpret_cast<const uint4*>(dc + (size_t)(r0 + i) * (inter / 2))[pp * 64 + lane];
-      sc[i][p] = ds[(size_t)(r0 + i) * (inter / G) + pp * 16 + (lane >> 2)];
+    for (int e = 0; e < 8; ++e) {
+      cb[e] = b[8 * j + e];
+      part += bf16_bits_to_f32(cb[e]);
     }
-  for (int t0 = 0; t0 < n; t0 += DD_TC) {
-    const int tc = min(DD_TC, n - t0);
-    wg_sync();   // the previous chunk's readers are done
-    for (int i = threadIdx.x; i < tc * q4; i += DD_NT) {
-      const int tt = i / q4, q = i - tt * q4;   // float4 q of token tt: k = 4 q
-      const int p = q >> 9, L = (q >> 3) & 63, j = q & 7;
-      hb[tt][(p * 8 + j) * 64 + L] = reinterpret_cast<const float4*>(h + (size_t)(t0 + tt) * inter)[q];
-    }
-    wg_sync();
-    for (int i = threadIdx.x; i < tc * P * 64; i += DD_NT) {
-      const int tt = i / (P * 64), pl = i - tt * (P * 64), p = pl >> 6, L = pl & 63;
-      float s = 0.f;
+    at[t][lane + 64 * j] = pack_pair_order(cb);
+    part = row16_sum(part);
+    if ((lane & 15) == 0) R[t][4 * j + (lane >> 4)] = part;
+  }
+}
+
+// Where some fp32 quotient lands on a bf16 midpoint: every value of the lane
+// from the correctly rounded quotient near midpoints (rare; kept out of line
+// so that the common path keeps few registers).
+__device__ __noinline__ void wave_block_input_exact(const float* __restrict__ xt, double ms, double rinv, int t,
+                                                    uint4 (*at)[DG_ROW], float (*R)[H / G]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t b[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float4 v = hb[tt][(p * 8 + j) * 64 + L];
-        s += ((v.x + v.y) + v.z) + v.w;
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double v = xt[8 * (lane + 64 * j) + e];
+      double q = v * rinv;
+      if (near_bf16_midpoint(q)) q = v / sqrt(ms);
+      b[8 * j + e] = f64_to_bf16_rne(q);
+    }
+  wave_block_input_store(b, t, at, R);
+}
+
+__device__ __forceinline__ void load_x_chunks(const float* __restrict__ xt, float4 (&xv)[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    xv[2 * j] = reinterpret_cast<const float4*>(xt)[2 * (lane + 64 * j)];
+    xv[2 * j + 1] = reinterpret_cast<const float4*>(xt)[2 * (lane + 64 * j) + 1];
+  }
+}
+
+__device__ __forceinline__ void wave_block_input(const float4 (&xv)[8], const float* __restrict__ xt, int t,
+                                                 uint4 (*at)[DG_ROW], float (*R)[H / G]) {
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const double v[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fma(v[e], v[e], ss);
+  }
+  ss = wave_sum(ss);
+  const double ms = ss / (double)H + RMS_EPS;
+  const double rinv = rsqrt(ms);
+  uint32_t b[32];
+  bool hard = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float qf = (float)((double)v[e] * rinv);
+      hard |= f32_on_bf16_midpoint(qf);
+      b[4 * j + e] = f32_to_bf16_rne(qf);
+    }
+  }
+  if (__builtin_expect(__ballot(hard) != 0ull, 0))   // wave-uniform
+    wave_block_input_exact(xt, ms, rinv, t, at, R);
+  else
+    wave_block_input_store(b, t, at, R);
+}
+
+// Gate/up: h[t][r] = silu(Wg[r] . a_t) * (Wu[r] . a_t).  Workgroup b owns rows
+// 16 b .. 16 b + 15; wave w takes K-groups 2 w and 2 w + 1 of both matrices
+// (lane l: row l % 16, the 32 elements 32 (l / 16) .. + 31 of each group).
+// Its codes are requested before the block inputs are formed (wave w forms
+// tokens w and w + 8); the 8 waves' partial sums are added in wave order.
+struct DenseGateUpLds {
+  union {
+    uint4 at[DENSE_MAX_TOKENS][DG_ROW];  // block inputs: chunk c of token t
+    float4 red[NWAVES][2][64];           // partial results of each wave (gate, up)
+  };
+  float R[DENSE_MAX_TOKENS][H / G];
+};
+
+__global__ void __launch_bounds__(NT, 4) k_dense_gateup(const float* __restrict__ x, int n,
+                                                        const uint8_t* __restrict__ gate,
+                                                        const uint16_t* __restrict__ gate_s,
+                                                        const uint8_t* __restrict__ up,
+                                                        const uint16_t* __restrict__ up_s, int rows,
+                                                        float* __restrict__ h) {
+  __shared__ DenseGateUpLds L;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, q = lane >> 4;
+  const size_t row = (size_t)blockIdx.x * 16 + col;
+  // this wave's first token (w, or n - 1 when w >= n) before the codes: the
+  // norm then waits for its own loads only (loads complete in issue order)
+  float4 xv[8];
+  load_x_chunks(x + (size_t)min(w, n - 1) * H, xv);
+  uint4 cg[2], cu[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    cg[i] = reinterpret_cast<const uint4*>(gate + row * (H / 2))[(2 * w + i) * 4 + q];
+    cu[i] = reinterpret_cast<const uint4*>(up + row * (H / 2))[(2 * w + i) * 4 + q];
+  }
+  const uint32_t sg = reinterpret_cast<const uint32_t*>(gate_s + row * (H / G))[w];   // groups 2w, 2w+1
+  const uint32_t su = reinterpret_cast<const uint32_t*>(up_s + row * (H / G))[w];
+  if (w < n) {   // wave-uniform
+    wave_block_input(xv, x + (size_t)w * H, w, L.at, L.R);
+  } else {
+    // a use on this path too, so the loads above stay ahead of the codes'
+    // instead of moving into the branch that normalises
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" ::"v"(xv[j].x), "v"(xv[j].y), "v"(xv[j].z), "v"(xv[j].w));
+  }
+  if (w + 8 < n) {   // wave-uniform
+    load_x_chunks(x + (size_t)(w + 8) * H, xv);
+    wave_block_input(xv, x + (size_t)(w + 8) * H, w + 8, L.at, L.R);
+  }
+  wg_sync();
+  // operands first (reads are unconditional; lanes of tokens past n take zeros)
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  uint4 a[2][4];
+  float Rg[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint4 v = L.at[col][16 * (2 * w + i) + 4 * q + st];
+      a[i][st] = col < n ? v : zero4;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = L.R[4 * q + r][2 * w + i];
+      Rg[i][r] = 4 * q + r < n ? v : 0.f;
+    }
+  }
+  // four independent accumulation chains: (group, matrix)
+  dn_f32x4 tg[2], tu[2];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t wg = st == 0 ? cg[i].x : st == 1 ? cg[i].y : st == 2 ? cg[i].z : cg[i].w;
+      const uint32_t wu = st == 0 ? cu[i].x : st == 1 ? cu[i].y : st == 2 ? cu[i].z : cu[i].w;
+      tg[i] = mfma16(a[i][st], expand8_o24(wg), st == 0 ? dn_f32x4{} : tg[i]);
+      tu[i] = mfma16(a[i][st], expand8_o24(wu), st == 0 ? dn_f32x4{} : tu[i]);
+    }
+  }
+  dn_f32x4 acc[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t s2 = m ? su : sg;
+    const float s0 = bf16_bits_to_f32(s2 & 0xFFFFu), s1 = bf16_bits_to_f32(s2 >> 16);
+    const dn_f32x4& t0 = m ? tu[0] : tg[0];
+    const dn_f32x4& t1 = m ? tu[1] : tg[1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[m][r] = fmaf(s0, t0[r], -24.f * s0 * Rg[0][r]) + fmaf(s1, t1[r], -24.f * s1 * Rg[1][r]);
+  }
+  wg_sync();   // every wave is done with the block inputs
+#pragma unroll
+  for (int m = 0; m < 2; ++m) L.red[w][m][lane] = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+  wg_sync();
+  if (threadIdx.x < 256) {
+    const int c = threadIdx.x & 15, t = threadIdx.x >> 4;
+    if (t < n) {
+      const int l = 16 * (t >> 2) + c, r = t & 3;
+      float gsum = 0.f, usum = 0.f;
+#pragma unroll
+      for (int v = 0; v < NWAVES; ++v) {
+        gsum += reinterpret_cast<const float*>(&L.red[v][0][l])[r];
+        usum += reinterpret_cast<const float*>(&L.red[v][1][l])[r];
       }
-      hsum[tt][pl] = s;
+      h[(size_t)t * rows + (size_t)blockIdx.x * 16 + c] = silu_mul(gsum, usum);
     }
-    wg_sync();
-    for (int tt = 0; tt < tc; ++tt) {
-      // keep the codes' conversions inside the token loop (hoisted, the
-      // converted values of all rows and passes would not fit in registers)
+  }
+}
+
+// Down: out[t][c] = x[t][c] + Wd[c] . h_t, K = inter = 128 NG.  Workgroup b
+// owns rows 16 b .. 16 b + 15; wave w takes the K-groups w, w + 8, w + 16, ...
+// in that order, whatever the call's size, so every token's arithmetic is the
+// same for any n.  h is fp32: the workgroup splits the h values of the call's
+// tokens into three bf16 parts (v = p0 + p1 + p2 exactly: each part takes the
+// next 8 significant bits) and stages them in LDS, a slice of 8 GW K-groups at
+// a time (GW groups per wave; fewer, larger slices when fewer tokens need
+// room); the 16 threads that stage one group of one token also form its sum R
+// with a row tree.  In the MFMA each token takes four rows of A (its three
+// parts and a zero row), so one instruction serves four tokens and a token's
+// three part sums come out in one lane, where they are added in part order;
+// the 8 waves' partial sums are added in wave order.  Thread i
+// stages the (token, chunk) pairs i + 512 m, tokens 0 .. 4 NI - 1 (NI =
+// ceil(n / 4)), and requests the h of DEPTH slices ahead; its loads are
+// unconditional (tokens past n re-read token n - 1), so each wait counts
+// exactly the loads issued after the ones it needs.
+constexpr int dd_gw(int ng, int ni) {   // K-groups per wave per slice
+  const int cand[5] = {6, 4, 3, 2, 1};
+  for (int g : cand)
+    if (ng % (8 * g) == 0 && 3 * (4 * ni) * (128 * g + 1) * 16 <= 100 * 1024) return g;
+  return 1;
+}
+
+template <int TC, int CH>   // staged tokens, 8-element chunks per token per slice
+struct DenseDownLds {
+  union {
+    uint4 hp[3][TC][CH + 1];   // chunk c of token t, part p (rows padded onto other banks)
+    float red[NWAVES][TC / 4][64];
+  };
+  float R[TC][CH / 16];         // per K-group of the slice: sum of the token's h
+};
+
+template <int NG, int NI>   // K-groups (inter / 128); (token, chunk) pairs per thread and group-slice column
+__global__ void __launch_bounds__(NT, 1) k_dense_down(const float* __restrict__ h, int n,
+                                                      const uint8_t* __restrict__ down,
+                                                      const uint16_t* __restrict__ down_s, const float* x,
+                                                      float* out) {
+  constexpr int inter = NG * G;
+  constexpr int GW = dd_gw(NG, NI);               // groups per wave per slice
+  constexpr int NSL = NG / (8 * GW);              // slices
+  constexpr int TC = 4 * NI;                      // tokens with room in LDS
+  constexpr int CH = 128 * GW;                    // chunks per token per slice
+  constexpr int IT = NI * GW;                     // (token, chunk) pairs per thread per slice
+  constexpr int DEPTH = NSL < 16 / IT ? NSL : (16 / IT > 0 ? 16 / IT : 1);   // slices in flight
+  static_assert(TC * CH == NT * IT, "pairs per slice");
+  __shared__ DenseDownLds<TC, CH> L;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, q = lane >> 4;
+  const size_t row = (size_t)blockIdx.x * 16 + col;
+  // codes and scale of this wave's K-groups w + 8 k, k < NG / 8
+  constexpr int KW = NG / 8;
+  uint4 code[KW];
+  float sc[KW];
 #pragma unroll
-      for (int i = 0; i < DD_ROWS; ++i)
+  for (int k = 0; k < KW; ++k) {
+    const int g = 8 * k + w;
+    code[k] = reinterpret_cast<const uint4*>(down + row * (inter / 2))[g * 4 + q];
+    sc[k] = bf16_bits_to_f32(down_s[row * (inter / G) + g]);
+  }
+  float4 hv[DEPTH][IT][2];
+  auto load_h = [&](int s, float4 (&buf)[IT][2]) {
 #pragma unroll
-        for (int p = 0; p < DD_PMAX; ++p)
-          asm volatile("" : "+v"(code[i][p].x), "+v"(code[i][p].y), "+v"(code[i][p].z), "+v"(code[i][p].w));
-      float acc[DD_ROWS] = {};
+    for (int m = 0; m < IT; ++m) {
+      const int j = threadIdx.x + NT * m, t = min(j / CH, n - 1), c = j % CH;
+      const float4* p = reinterpret_cast<const float4*>(h + (size_t)t * inter + (size_t)CH * 8 * s + 8 * c);
+      buf[m][0] = p[0];
+      buf[m][1] = p[1];
+    }
+  };
 #pragma unroll
-      for (int p = 0; p < DD_PMAX; ++p) {
-        if (p < P) {
-          float4 h4[8];
+  for (int s = 0; s < DEPTH; ++s) load_h(s, hv[s]);
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  float acc[NI] = {};   // token 4 tg + q, column col
 #pragma unroll
-          for (int j = 0; j < 8; ++j) h4[j] = hb[tt][(p * 8 + j) * 64 + lane];
-          const float hs = hsum[tt][p * 64 + lane];
+  for (int s = 0; s < NSL; ++s) {
+    float4 (&buf)[IT][2] = hv[s % DEPTH];
 #pragma unroll
-          for (int i = 0; i < DD_ROWS; ++i) acc[i] += lane_dot_down(code[i][p], h4, hs, bf16_bits_to_f32(sc[i][p]));
+    for (int m = 0; m < IT; ++m) {
+      const int j = threadIdx.x + NT * m, t = j / CH, c = j % CH;
+      float csum = 0.f;
+      if (t < n) {
+        const float e[8] = {buf[m][0].x, buf[m][0].y, buf[m][0].z, buf[m][0].w,
+                            buf[m][1].x, buf[m][1].y, buf[m][1].z, buf[m][1].w};
+        uint32_t b0[8], b1[8], b2[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          b0[k] = f32_to_bf16_rne(e[k]);
+          const float r1 = e[k] - bf16_bits_to_f32(b0[k]);
+          b1[k] = f32_to_bf16_rne(r1);
+          b2[k] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1[k]));
         }
+        L.hp[0][t][c] = pack_pair_order(b0);
+        L.hp[1][t][c] = pack_pair_order(b1);
+        L.hp[2][t][c] = pack_pair_order(b2);
+        csum = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
+      csum = row16_sum(csum);   // the 16 threads of a row: one K-group of one token
+      if ((c & 15) == 0 && t < n) L.R[t][c >> 4] = csum;
+    }
+    if (s + DEPTH < NSL) load_h(s + DEPTH, buf);
+    wg_sync();
 #pragma unroll
-      for (int i = 0; i < DD_ROWS; ++i) {
-        const float v = wave_sum(acc[i]);
-        if (lane == 0) {
-          const size_t o = (size_t)(t0 + tt) * H + r0 + i;
-          out[o] = x[o] + v;
+    for (int gi = 0; gi < GW; ++gi) {
+      const int gl = 8 * gi + w;   // K-group of the slice
+      const int k = s * GW + gi;   // this wave's k-th K-group: w + 8 k
+      const uint32_t cw[4] = {code[k].x, code[k].y, code[k].z, code[k].w};
+      uint4 bw[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) bw[st] = expand8_o24(cw[st]);
+#pragma unroll
+      for (int tg = 0; tg < NI; ++tg) {
+        // rows of the MFMA's A: 4 per token (parts 0, 1, 2 and a zero row);
+        // lane l holds row l % 16 = 4 (token % 4) + part
+        const int t = 4 * tg + (col >> 2), part = col & 3;
+        uint4 a[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const uint4 v = L.hp[part < 3 ? part : 0][t][16 * gl + 4 * q + st];
+          a[st] = (t < n && part < 3) ? v : zero4;
         }
+        dn_f32x4 d = mfma16(a[0], bw[0], dn_f32x4{});
+#pragma unroll
+        for (int st = 1; st < 4; ++st) d = mfma16(a[st], bw[st], d);
+        // D rows 4 q + r: token 4 tg + q, part r
+        const int tq = 4 * tg + q;
+        const float Rt = tq < n ? L.R[tq][gl] : 0.f;
+        acc[tg] += fmaf(sc[k], (d[0] + d[1]) + d[2], -24.f * sc[k] * Rt);
       }
     }
+    wg_sync();   // the next slice's staging (or the partial sums) must not overtake these reads
+  }
+  float xo = 0.f;
+  const int oc = threadIdx.x & 15, ot = threadIdx.x >> 4;
+  const bool writer = threadIdx.x < 256 && ot < n;
+  const size_t o = (size_t)ot * H + (size_t)blockIdx.x * 16 + oc;
+  if (writer) xo = x[o];
+#pragma unroll
+  for (int tg = 0; tg < NI; ++tg) L.red[w][tg][lane] = acc[tg];
+  wg_sync();
+  if (writer) {
+    const int tg = ot >> 2, l = 16 * (ot & 3) + oc;
+    float y = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWAVES; ++v) y += L.red[v][tg][l];
+    out[o] = xo + y;
+  }
+}
+
+template <int NG>
+static void launch_dense_down(int n, const float* h, const uint8_t* down, const uint16_t* down_s, const float* x,
+                              float* out, hipStream_t s) {
+  const dim3 grid(H / 16), block(NT);
+  switch ((n + 3) / 4) {
+    case 1: hipLaunchKernelGGL((k_dense_down<NG, 1>), grid, block, 0, s, h, n, down, down_s, x, out); break;
+    case 2: hipLaunchKernelGGL((k_dense_down<NG, 2>), grid, block, 0, s, h, n, down, down_s, x, out); break;
+    case 3: hipLaunchKernelGGL((k_dense_down<NG, 3>), grid, block, 0, s, h, n, down, down_s, x, out); break;
+    default: hipLaunchKernelGGL((k_dense_down<NG, 4>), grid, block, 0, s, h, n, down, down_s, x, out); break;
   }
 }
 
@@ -376,9 +577,13 @@ hipError_t launch_dense_mlp(const uint8_t* gate, const uint16_t* gate_s, const u
                             float* out, hipStream_t s) {
   if (n < 1 || n > DENSE_MAX_TOKENS || inter < 2048 || inter > FLINT_DENSE_MLP_SIZE || inter % 2048)
     return hipErrorInvalidValue;
-  const int grid = std::min(DN_GRID, (inter + NWAVES - 1) / NWAVES);
-  hipLaunchKernelGGL((k_rows_k2048<true, 4>), dim3(grid), dim3(NT), 0, s, x, n, gate, gate_s, up, up_s, inter, h);
-  hipLaunchKernelGGL(k_dense_down, dim3(DD_GRID), dim3(DD_NT), 0, s, h, n, inter, down, down_s, x, out);
+  hipLaunchKernelGGL(k_dense_gateup, dim3(inter / 16), dim3(NT), 0, s, x, n, gate, gate_s, up, up_s, inter, h);
+  if (inter == 2048)
+    launch_dense_down<16>(n, h, down, down_s, x, out, s);
+  else if (inter == 4096)
+    launch_dense_down<32>(n, h, down, down_s, x, out, s);
+  else
+    launch_dense_down<48>(n, h, down, down_s, x, out, s);
   return hipGetLastError();
 }
 

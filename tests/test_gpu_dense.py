@@ -172,3 +172,40 @@ def test_writes_stay_inside_outputs(head, dense):
     h_ref, out_ref = run_dense(inter, w, x.cpu().numpy())
     assert np.array_equal(h[: 3 * inter].view(torch.float32).view(3, inter).cpu().numpy(), h_ref)
     assert np.array_equal(out[: 3 * H].view(torch.float32).view(3, H).cpu().numpy(), out_ref)
+
+
+def _pack_rows(codes):
+    """int4 codes [rows][K] in [-8, 7] -> bytes [rows][K/2], even k in the low nibble."""
+    c = (np.asarray(codes, np.int64) & 0xF).astype(np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_dense_mlp_block_input_at_bf16_midpoints():
+    """A residual whose normalised values are exact and land on (and next to)
+    bf16 rounding midpoints, so the block input takes its exact-quotient path.
+    Gate and up rows r < 16 pick element r alone (code 1, scale 1), so h_r =
+    silu(a_r) a_r shows a_r itself: one bf16 step in a_r (2^-8 relative)
+    moves h_r by far more than the bound used here."""
+    from test_oracle_stack_pins import _crafted_residual
+    x, _ = _crafted_residual()
+    inter = 2048
+    gu = np.zeros((inter, H), np.int64)
+    gu[np.arange(16), np.arange(16)] = 1
+    one = np.full((inter, H // FL.group), 0x3F80, np.int16)   # scale 1.0
+    dn = fg.dense_layer(0, 1, inter=inter)
+    wc = {"gate": _pack_rows(gu), "gate_s": one, "up": _pack_rows(gu), "up_s": one,
+          "down": dn["down"].numpy(), "down_s": dn["down_s"].numpy()}
+    w = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in wc.items()}
+    xs = np.stack([x, fg.token(6, 0)])   # a second, ordinary token in the same call
+    h, out = run_dense(inter, w, xs)
+    res = O.dense_mlp(x, wc, FL)
+    a = O.block_input(x, FL)
+    assert np.all(np.abs(h[0, :16] - res.h[:16]) <= 2e-4), np.abs(h[0, :16] - res.h[:16]).max()
+    # a one-step error in any of the first 16 activations would exceed the bound above
+    step = np.abs(a[:16]) * 2.0 ** -8
+    assert np.all(step * 0.9 > 2e-4 * 2)
+    d_gpu = out[0].astype(np.float64) - x
+    d_ref = res.x_out.astype(np.float64) - x
+    assert np.linalg.norm(d_gpu - d_ref) / np.linalg.norm(d_ref) <= REL_L2
+    h1, _ = run_dense(inter, w, xs[1:])
+    assert np.array_equal(h1[0], h[1])
