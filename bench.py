@@ -310,7 +310,8 @@ def bench_cost_table(args):
     stream = torch.cuda.current_stream()
     batches = 4                         # distinct token batches per n, used in turn
     rows = []
-    for n in range(1, cap + 1):
+    ns = [int(v) for v in args.cost_table_tokens.split(",")] if args.cost_table_tokens else range(1, cap + 1)
+    for n in ns:
         xs = [pool[b * 16:b * 16 + n] for b in range(batches)]
         # distinct experts per layer of each batch, from one traced call
         model.set_trace(ids, wts, cap)
@@ -804,6 +805,8 @@ def _main():
                     help="time the decode attention with sinks instead (full layer at 100,000 positions, window layer)")
     ap.add_argument("--attn-batch1", action="store_true",
                     help="with --attn: only the batch-1 full layer (for a kernel trace of that one shape)")
+    ap.add_argument("--cost-table-tokens", default=None,
+                    help="comma-separated token counts for --cost-table (default 1..16)")
     ap.add_argument("--phase-table", action="store_true",
                     help="decode phase timestamps (needs the --phase-ts build of the library)")
     ap.add_argument("--phase-table-out", default=None, help="write the phase table to this file")
