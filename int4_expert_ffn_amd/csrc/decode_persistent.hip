@@ -22,6 +22,9 @@
 // so both launch modes give bitwise-identical results.
 #include <hip/hip_fp16.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "decode_common.h"
 #include "decode_persistent.h"
 
@@ -617,6 +620,12 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
   wg_sync();
 
   for (int l = A.l0; l < A.l1; ++l) {
+    // thread indices recomputed from an opaque copy each layer, so that the
+    // compiler does not hoist addresses derived from them out of the layer
+    // loop (held across it, they would not fit in registers and be spilled)
+    int tid_l = threadIdx.x;
+    asm volatile("" : "+v"(tid_l));
+    const int tid = tid_l, wave = tid_l >> 6, lane = tid_l & 63;
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
     // router rows of this workgroup: requested before the x exchange
@@ -688,10 +697,15 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
     {
       // task j: j < NSH shared row NSH u + j, else routed row q = NRT u + j - NSH
       // of the token's experts in pick order (slot q / I, row q % I); task j
-      // goes to wave j % 8, TB tasks in flight per wave
-      constexpr int TB = K >= 4 ? 4 : 2;
-      uint4 qg[TB], qu[TB];
-      uint32_t qsg[TB], qsu[TB];
+      // goes to wave j % 8.  Batches of TB tasks in two register sets: the
+      // next batch's rows are requested before the current one is computed.
+      // Loads are unconditional (tasks past the last re-read it), so each
+      // wait counts exactly the loads issued after the ones it needs.
+      constexpr int TB = 2;
+      struct Batch {
+        uint4 qg[TB], qu[TB];
+        uint32_t qsg[TB], qsu[TB];
+      };
       auto task_row = [&](int j, const uint8_t*& g, const uint16_t*& gs, const uint8_t*& up, const uint16_t*& us,
                           size_t& rr) {
         if (j < NSH) {
@@ -703,38 +717,44 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
           g = L.gate; gs = L.gate_s; up = L.up; us = L.up_s;
         }
       };
-      auto load_batch = [&](int j0) {
+      auto load_batch = [&](int j0, Batch& bt) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
-          const int j = j0 + b * NWAVES;
-          if (j < NTASK) {
-            const uint8_t *g, *up;
-            const uint16_t *gs, *us;
-            size_t rr;
-            task_row(j, g, gs, up, us, rr);
-            qg[b] = reinterpret_cast<const uint4*>(g + rr * (H / 2))[lane];
-            qu[b] = reinterpret_cast<const uint4*>(up + rr * (H / 2))[lane];
-            qsg[b] = gs[rr * (H / G) + (lane >> 2)];
-            qsu[b] = us[rr * (H / G) + (lane >> 2)];
-          }
+          const int j = min(j0 + b * NWAVES, NTASK - 1);
+          const uint8_t *g, *up;
+          const uint16_t *gs, *us;
+          size_t rr;
+          task_row(j, g, gs, up, us, rr);
+          bt.qg[b] = reinterpret_cast<const uint4*>(g + rr * (H / 2))[lane];
+          bt.qu[b] = reinterpret_cast<const uint4*>(up + rr * (H / 2))[lane];
+          bt.qsg[b] = gs[rr * (H / G) + (lane >> 2)];
+          bt.qsu[b] = us[rr * (H / G) + (lane >> 2)];
         }
       };
-      auto compute_batch = [&](int j0) {
+      auto compute_batch = [&](int j0, const Batch& bt) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
           const int j = j0 + b * NWAVES;
           if (j >= NTASK) break;
           const int word = j < NSH ? TOPK * I + NSH * u + j : NRT * u + (j - NSH);   // slot * I + row
-          const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
+          const float hv = gateup_row_token(bt.qg[b], bt.qsg[b], bt.qu[b], bt.qsu[b], a_lds, asum_lds[lane]);
           if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
             hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
             hloc_idx[j] = word;
           }
         }
       };
-      for (int j0 = wave; j0 < NTASK; j0 += TB * NWAVES) {
-        load_batch(j0);
-        compute_batch(j0);
+      // NTASK / 8 = 2 K tasks per wave: an even number of batches of 2
+      static_assert((NTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
+      Batch ba, bb;
+      load_batch(wave, ba);
+#pragma unroll
+      for (int k = 0; k < NTASK / NWAVES / (2 * TB); ++k) {
+        const int j0 = wave + k * 2 * TB * NWAVES;
+        load_batch(j0 + TB * NWAVES, bb);
+        compute_batch(j0, ba);
+        load_batch(j0 + 2 * TB * NWAVES, ba);   // past the last task: a cached re-read, never used
+        compute_batch(j0 + TB * NWAVES, bb);
       }
     }
     wg_sync();
@@ -848,6 +868,12 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
   wg_sync();
 
   for (int l = A.l0; l < A.l1; ++l) {
+    // thread indices recomputed from an opaque copy each layer, so that the
+    // compiler does not hoist addresses derived from them out of the layer
+    // loop (held across it, they would not fit in registers and be spilled)
+    int tid_l = threadIdx.x;
+    asm volatile("" : "+v"(tid_l));
+    const int tid = tid_l, wave = tid_l >> 6, lane = tid_l & 63;
     const LayerW L = layer_at(A.base, A.layer_stride, l);
     const uint32_t tag = A.epoch + ((uint32_t)l << 2);
     // router rows of this workgroup: requested before the x exchange
@@ -918,41 +944,53 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
     {
       // task j: j < nsh shared row s0 + j, else routed row q = q0 + j - nsh of
       // the token's experts in pick order (slot q / I, row q % I); task j goes
-      // to wave j % 8, TB tasks in flight per wave
-      constexpr int TB = K >= 4 ? 4 : 2;
-      uint4 qg[TB], qu[TB];
-      uint32_t qsg[TB], qsu[TB];
-      auto load_batch = [&](int j0) {
+      // to wave j % 8.  Batches of TB tasks in two register sets: the next
+      // batch's rows are requested before the current one is computed.  The
+      // loop runs the most batches any workgroup has (a fixed count), its loads
+      // unconditional (tasks past the last re-read it), so each wait counts
+      // exactly the loads issued after the ones it needs.
+      constexpr int TB = 2;
+      struct Batch {
+        uint4 qg[TB], qu[TB];
+        uint32_t qsg[TB], qsu[TB];
+      };
+      auto load_batch = [&](int j0, Batch& bt) {
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+          const int j = min(j0 + b * NWAVES, ntask - 1);
+          const bool sh = j < nsh;
+          const int q = q0 + (j - nsh);
+          const size_t rr = sh ? (size_t)(s0 + j) : (size_t)ids_l[q / I] * I + (q % I);
+          bt.qg[b] = reinterpret_cast<const uint4*>((sh ? L.sh_gate : L.gate) + rr * (H / 2))[lane];
+          bt.qu[b] = reinterpret_cast<const uint4*>((sh ? L.sh_up : L.up) + rr * (H / 2))[lane];
+          bt.qsg[b] = (sh ? L.sh_gate_s : L.gate_s)[rr * (H / G) + (lane >> 2)];
+          bt.qsu[b] = (sh ? L.sh_up_s : L.up_s)[rr * (H / G) + (lane >> 2)];
+        }
+      };
+      auto compute_batch = [&](int j0, const Batch& bt) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
           const int j = j0 + b * NWAVES;
-          if (j < ntask) {
-            const bool sh = j < nsh;
-            const int q = q0 + (j - nsh);
-            const size_t rr = sh ? (size_t)(s0 + j) : (size_t)ids_l[q / I] * I + (q % I);
-            qg[b] = reinterpret_cast<const uint4*>((sh ? L.sh_gate : L.gate) + rr * (H / 2))[lane];
-            qu[b] = reinterpret_cast<const uint4*>((sh ? L.sh_up : L.up) + rr * (H / 2))[lane];
-            qsg[b] = (sh ? L.sh_gate_s : L.gate_s)[rr * (H / G) + (lane >> 2)];
-            qsu[b] = (sh ? L.sh_up_s : L.up_s)[rr * (H / G) + (lane >> 2)];
+          if (j < ntask) {   // wave-uniform
+            const int word = j < nsh ? TOPK * I + s0 + j : q0 + (j - nsh);   // slot * I + row
+            const float hv = gateup_row_token(bt.qg[b], bt.qsg[b], bt.qu[b], bt.qsu[b], a_lds, asum_lds[lane]);
+            if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
+              hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
+              hloc_idx[j] = word;
+            }
           }
         }
       };
-      auto compute_batch = [&](int j0) {
+      static_assert((MTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
+      Batch ba, bb;
+      load_batch(wave, ba);
 #pragma unroll
-        for (int b = 0; b < TB; ++b) {
-          const int j = j0 + b * NWAVES;
-          if (j >= ntask) break;
-          const int word = j < nsh ? TOPK * I + s0 + j : q0 + (j - nsh);   // slot * I + row
-          const float hv = gateup_row_token(qg[b], qsg[b], qu[b], qsu[b], a_lds, asum_lds[lane]);
-          if (lane == 0) {   // in task order: the publisher's lanes write consecutive words
-            hloc[j] = F16H ? __half2float(__float2half_rn(hv)) : hv;
-            hloc_idx[j] = word;
-          }
-        }
-      };
-      for (int j0 = wave; j0 < ntask; j0 += TB * NWAVES) {
-        load_batch(j0);
-        compute_batch(j0);
+      for (int k = 0; k < MTASK / NWAVES / (2 * TB); ++k) {
+        const int j0 = wave + k * 2 * TB * NWAVES;
+        load_batch(j0 + TB * NWAVES, bb);
+        compute_batch(j0, ba);
+        load_batch(j0 + 2 * TB * NWAVES, ba);   // past the last task: a cached re-read, never used
+        compute_batch(j0 + TB * NWAVES, bb);
       }
     }
     wg_sync();
@@ -988,15 +1026,16 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
 #pragma unroll
       for (int i = 0; i < K; ++i) {   // nout <= 8 K
         const int lr = wave + NWAVES * i;   // local output row
-        if (lr >= nout) break;
-        uint4 nca = ca, ncb = cb;
-        uint32_t nsa = sa, nsb = sb;
-        if (lr + NWAVES < nout) load_down_row(L, ids_l, o0 + lr + NWAVES, nca, nsa, ncb, nsb);
-        float v;
-        if constexpr (F16H) v = down_row_token(ca, sa, cb, sb, load_a, load_b, wsc, xown[lr]);
-        else v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
-        if (lane == 0) xnew[lr] = v;
-        ca = nca; cb = ncb; sa = nsa; sb = nsb;
+        if (lr < nout) {   // wave-uniform; no break, so the loop unrolls
+          uint4 nca = ca, ncb = cb;
+          uint32_t nsa = sa, nsb = sb;
+          if (lr + NWAVES < nout) load_down_row(L, ids_l, o0 + lr + NWAVES, nca, nsa, ncb, nsb);
+          float v;
+          if constexpr (F16H) v = down_row_token(ca, sa, cb, sb, load_a, load_b, wsc, xown[lr]);
+          else v = down_row_token(ca, sa, cb, sb, load_a, load_b, w_l, xown[lr]);
+          if (lane == 0) xnew[lr] = v;
+          ca = nca; cb = ncb; sa = nsa; sb = nsb;
+        }
       }
     }
     wg_sync();
@@ -1035,11 +1074,17 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   void* kargs[] = {&a};
   // One token: the schedule above.  Otherwise groups for K tokens, K the
   // power of two at or above n: the statically sized kernel leaves K - n
-  // groups idle, the exact-range kernel uses every workgroup but runs about
-  // a quarter slower per row; measured, the exact ranges win when n < 0.7 K.
+  // groups idle, the exact-range kernel uses every workgroup; measured, the
+  // exact ranges win up to n = 0.75 K.
   const int n = a.n;
   const int K = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
-  const bool exact = 10 * n < 7 * K;
+  // FLINT_MOE_GROUPS=exact or =pow2 forces one form for every n that is not a
+  // power of two (for measuring the rule below)
+  static const int force = [] {
+    const char* v = getenv("FLINT_MOE_GROUPS");
+    return !v ? 0 : strcmp(v, "exact") == 0 ? 1 : strcmp(v, "pow2") == 0 ? 2 : 0;
+  }();
+  const bool exact = force == 1 ? n != K : force == 2 ? false : 4 * n <= 3 * K;
   const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact) : decode_kernel<false>(K, exact);
   return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
 }
