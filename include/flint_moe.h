@@ -88,7 +88,9 @@ typedef struct {
  * on the current HIP device.  Synchronous: the weights are copied into memory
  * the library owns, so the caller may free its buffers when the call returns.
  * `weights` is a host array of n_layers descriptors of device pointers.
- * On failure *out is set to NULL and nothing is leaked. */
+ * On failure *out is set to NULL and nothing is leaked.  Test hook: with the
+ * environment variable FLINT_MOE_FAIL_ALLOC=k (k >= 1), the k-th device
+ * allocation of the call fails with FLINT_ERR_OUT_OF_MEMORY. */
 int flint_moe_create(const flint_moe_layer* weights, int n_layers, flint_moe_t* out);
 
 /* Create a handle for weights in the fp16-intermediate pack form (TandemLLM

@@ -98,11 +98,17 @@ static void release(flint_moe* h) {
   delete h;
 }
 
+// Test hook: FLINT_MOE_FAIL_ALLOC=k (k >= 1) makes the k-th device allocation
+// of a create call fail as if the device were out of memory, so that every
+// partial-release path of create can be exercised.
+static thread_local int g_alloc_count = 0;
+
 static int checked_malloc(void** p, size_t bytes, const char* what) {
   const char* inj = getenv("FLINT_MOE_FAIL_ALLOC");
-  if (inj && inj[0] == '1') {
+  if (inj && ++g_alloc_count == atoi(inj)) {
     *p = nullptr;
-    return fail(FLINT_ERR_OUT_OF_MEMORY, "allocation of %zu bytes for %s failed (injected)", bytes, what);
+    return fail(FLINT_ERR_OUT_OF_MEMORY, "allocation %d (%zu bytes for %s) failed (injected)", g_alloc_count,
+                bytes, what);
   }
   hipError_t e = hipMalloc(p, bytes);
   if (e != hipSuccess) {
@@ -140,6 +146,7 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
       if (!ptrs[i]) return fail(FLINT_ERR_INVALID_ARG, "layer %d: tensor %d is NULL", l, i);
   }
   flint_moe* h = new flint_moe();
+  g_alloc_count = 0;
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { int r = fail_hip(e, "hipGetDevice"); h->device = -1; release(h); return r; }
   h->n_layers = n_layers;

@@ -148,16 +148,40 @@ def test_invalid_arguments_rejected(model):
     m.status()
 
 
-def test_allocation_failure_is_reported(model):
+CREATE_ALLOCATIONS = 10   # device allocations of one create call
+
+
+def test_allocation_failure_is_reported_and_releases_everything(model):
+    """Create failing at each of its device allocations in turn: the error is
+    reported, and what the call had allocated until then is freed (device
+    memory returns to exactly its level before the call)."""
     synth, m, ids, w = model
     layers = build_layers(fg.Synth(FL, seed=1, n_layers=1), [0])
-    os.environ["FLINT_MOE_FAIL_ALLOC"] = "1"
+    torch.cuda.synchronize()
+    F.FlintMoE(layers).close()          # a full create and destroy first, so lazy runtime set-up is done
+    torch.cuda.empty_cache()
+    free0 = torch.cuda.mem_get_info()[0]
     try:
-        with pytest.raises(F.FlintMoEError) as ei:
-            F.FlintMoE(layers)
-        assert ei.value.code == F.FLINT_ERR_OUT_OF_MEMORY
+        for k in range(1, CREATE_ALLOCATIONS + 1):
+            os.environ["FLINT_MOE_FAIL_ALLOC"] = str(k)
+            with pytest.raises(F.FlintMoEError) as ei:
+                F.FlintMoE(layers)
+            assert ei.value.code == F.FLINT_ERR_OUT_OF_MEMORY
+            assert f"allocation {k} " in str(ei.value)
+            assert torch.cuda.mem_get_info()[0] == free0, k
+        os.environ["FLINT_MOE_FAIL_ALLOC"] = str(CREATE_ALLOCATIONS + 1)   # past the last one: no failure
+        m2 = F.FlintMoE(layers)
     finally:
         del os.environ["FLINT_MOE_FAIL_ALLOC"]
+    x = torch.from_numpy(fg.tokens(0, [7])).cuda()
+    out = m2.forward(x, 0, 1)
+    torch.cuda.synchronize()
+    m2.status()
+    assert torch.isfinite(out).all()
+    m2.close()
+    del x, out
+    torch.cuda.empty_cache()            # the tensors of this test were torch's, not the library's
+    assert torch.cuda.mem_get_info()[0] == free0
 
 
 def test_persistent_and_layered_modes_agree_bitwise(model):
