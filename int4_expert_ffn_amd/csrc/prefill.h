@@ -7,7 +7,7 @@
 
 namespace flint {
 
-constexpr int PF_TM = 64;                                   // tokens per GEMM tile (two 32-row MFMA blocks)
+constexpr int PF_TM = 32;                                   // (token, slot) pairs per routed GEMM tile
 constexpr int PF_BW = FLINT_MAX_TOKENS / 32;                // bitmap words per expert
 constexpr int PF_MAX_TILES = (FLINT_MAX_TOKENS * TOPK + PF_TM - 1) / PF_TM + E;
 
@@ -34,9 +34,19 @@ typedef int (*alloc_fn)(void** p, size_t bytes, const char* what);
 // Allocates the workspace in one block (*mem owns it).
 int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc);
 
+// Tile-major copy of a layer's int4 matrices, the layout the prefill GEMMs
+// stream: for rows 32 b .. 32 b + 31 of a matrix with K codes per row
+// (K / G groups), the codes of group g are two contiguous 1 KB runs
+// [b][g][i][lane][16 bytes], lane = 32 hl + r holding bytes 64 g + 32 hl + 16 i
+// of row 32 b + r, so that one 16-byte load per lane gives a wave the MFMA
+// operands of 32 rows; the scales are [b][g][r].  Each tensor keeps its
+// row-major size.  dst's router and bias are not used.
+hipError_t prefill_pack_layer(const LayerW& src, const LayerW& dst, hipStream_t s);
+
 // One layer for n tokens: out = x + moe(rmsnorm(x)).  out may equal xin.
+// L: the layer (router and bias are read from it), P: its tile-major copy.
 // trace_ids / trace_w (may be null) receive the picks and weights [n][TOPK].
-hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const PrefillWS& ws,
-                                int* trace_ids, float* trace_w, hipStream_t s);
+hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const LayerW& P,
+                                const PrefillWS& ws, int* trace_ids, float* trace_w, hipStream_t s);
 
 }  // namespace flint

@@ -1,14 +1,14 @@
 // Prefill path: a block of n tokens (DECODE_MAX_TOKENS < n <= FLINT_MAX_TOKENS)
 // through one layer, where the block becomes a dense contraction: ~48 tokens
 // per expert on average at n = 2048, so each expert's weights are read once
-// per 64-token tile and multiplied on the matrix cores.
+// per 32-row tile and multiplied on the matrix cores.
 //
 //   k_pf_input    block input a = bf16(rmsnorm(x)) per token (the decode's
 //                 rounding rule), 8-element chunks in pair order
 //   k_pf_router   z = a Wr^T, bf16 MFMA with fp32 accumulation
 //   k_pf_route    per token (one wave): s = sigmoid(z), c = s + b in fp64,
 //                 top-6 and weights; marks the token in each pick's bitmap
-//   k_pf_offsets  per-expert counts, their exclusive scan, the 64-token tiles
+//   k_pf_offsets  per-expert counts, their exclusive scan, the 32-row tiles
 //   k_pf_scatter  (token, slot) pairs in expert order, tokens increasing
 //                 within an expert (popcounts of the bitmap prefix)
 //   k_pf_gateup   routed gate/up + SwiGLU per tile (grouped GEMM)
@@ -49,8 +49,8 @@ __device__ __forceinline__ pf_f32x16 mfma_bf16(uint4 a, uint4 b, pf_f32x16 c) {
 // 8 int4 codes of one dword (k0 in bits 0-3) -> bf16 128 + n' in pair order
 // (k0, k2, k4, k6, k1, k3, k5, k7), n' = code + 8.
 __device__ __forceinline__ uint4 expand_codes(uint32_t code) {
-  const uint32_t x = code ^ 0x88888888u;
-  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  // (nibble ^ 8) of the low and the high nibbles: one and-xor each
+  const uint32_t lo = (code & 0x0F0F0F0Fu) ^ 0x08080808u, hi = ((code >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
   const uint32_t K43 = 0x43434343u;
   return make_uint4(__builtin_amdgcn_perm(K43, lo, 0x04010400u), __builtin_amdgcn_perm(K43, lo, 0x04030402u),
                     __builtin_amdgcn_perm(K43, hi, 0x04010400u), __builtin_amdgcn_perm(K43, hi, 0x04030402u));
@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(PF_NT) k_pf_route(const float* __restrict__ z,
 // on XCD b % 8 (round-robin dispatch); only speed depends on that.
 __device__ __forceinline__ int snake_rank(int x, int j) { return 16 * (j >> 1) + ((j & 1) ? 15 - x : x); }
 
-constexpr int PF_NT_BINS = FLINT_MAX_TOKENS / PF_TM + 1;   // tile counts 0..32 of one expert
+constexpr int PF_NT_BINS = FLINT_MAX_TOKENS / PF_TM + 1;   // tile counts 0..64 of one expert
 
 __global__ void __launch_bounds__(E) k_pf_offsets(const uint32_t* __restrict__ bitmap, int n, int* __restrict__ offsets,
                                                    int4* __restrict__ tiles, int* __restrict__ tile_start) {
@@ -268,203 +268,211 @@ __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ id
   perm[pos] = p;
 }
 
-// ------------------------------------------------------------- GEMM tile
-// One workgroup computes 64 tile rows (rows of A given by rows_lds[m]; -1 is
-// padding: computed from tile row 0, never stored) against NB x 32 weight rows
-// per wave starting at wrow0, for NMAT weight matrices that share A.
-// A: bf16 rows of lda elements in pair-order 8-element chunks, NSPLIT parts
-// whose sum is the operand.  W: int4 codes [rows][KG x 64 bytes], S: bf16
-// scales [rows][KG].  acc[mat][nb][mb] receives row block mb (tile rows
-// 32 mb ..) for columns nb x 32 + lane % 32 of this wave's rows.
+// ------------------------------------------------------------- resident-tile GEMM
+// One workgroup of PR_NT threads (8 waves) computes a tile of 32 A rows against
+// weight rows.  The whole tile, all of K, sits in LDS for the item, so the K
+// loop needs no barrier: each wave streams the int4 codes and scales of its
+// own weight rows through a ring of PR_D register sets (step = one K-group of
+// 32 rows of each weight matrix), the loads of step s + PR_D in flight while
+// step s runs on the matrix cores.
 //
-// Per K-group g the MFMAs accumulate sum_k (code_k + 136) a_k from zero, and
-// that is added to acc times the scale s[n][g].  The remaining
-// -136 sum_g s[n][g] R[m][g] (R: sums of A over each group) is one more MFMA
-// step at the end, with R split into three bf16 parts so its products are
-// exact.
-// LDS: a_lds [2][NSPLIT][2][16][32] uint4 (chunk c of tile row r at row
-// position r ^ (c & 14)), rsum_lds [64][KG] floats.
-template <int NB, int NMAT, int KG, int NSPLIT>
-__device__ __forceinline__ void gemm_tile(const uint16_t* const (&A)[NSPLIT], int lda, const int* rows_lds,
-                                          const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT],
-                                          int wrow0, pf_f32x16 (&acc)[NMAT][NB][2], uint4* a_lds, float* rsum_lds) {
-  const int tid = threadIdx.x, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
-  const int srow = tid >> 3, scp = tid & 7;   // staging: row, chunk pair
-  constexpr int KB = KG * 64;                 // code bytes per weight row
+// A: bf16 rows of K elements in pair-order 8-element chunks, NSPLIT parts
+// whose sum is the operand (the block input; or h as hi + lo).  W, S: int4
+// codes and bf16 scales in the tile-major layout (prefill.h).  The MFMA is 32 x 32 x 16
+// with the tile rows as M and 32 weight rows as N; in K-group g, step j, lane
+// half hl multiplies chunk 16 g + 8 hl + j (the lane's code dword j of its 32
+// bytes g * 64 + 32 hl of the row).
+//
+// Per K-group the MFMAs accumulate sum_k (code_k + 136) a_k from zero (exact
+// products, fp32), and that is added to acc times the scale s[n][g].  The
+// remaining -136 sum_g s[n][g] R[m][g] (R: the sums of A over each group) is
+// one more MFMA step per 32 x 32 block, with R split into three bf16 parts so
+// that its products are exact.
+constexpr int PR_TM = 32;    // A rows of a tile
+constexpr int PR_NT = 512;   // threads of the resident-tile kernels (8 waves)
+constexpr int PR_D = 2;      // steps of weight loads in flight per wave
 
-  // codes and scale bits of this lane's weight rows for one K-group
-  struct Codes {
-    uint4 c[NMAT][NB][2];
-    uint32_t s[NMAT][NB];
-  };
-  auto load_codes = [&](int g, Codes& d) {
-#pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const size_t wr = (size_t)(wrow0 + nb * 32 + lrow);
-        const uint4* p = reinterpret_cast<const uint4*>(W[mat] + wr * KB + g * 64 + hl * 32);
-        d.c[mat][nb][0] = p[0];
-        d.c[mat][nb][1] = p[1];
-        d.s[mat][nb] = S[mat][wr * KG + g];
-      }
-  };
-  // Loads are issued unconditionally so that the wave's memory counter can
-  // wait for the A tile without waiting for the younger code loads: padding
-  // rows read tile row 0, and the last group is re-read.
-  uint4 stg[NSPLIT][2][2];
-  auto stage_load = [&](int g) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int r = rows_lds[mb * 32 + srow];
-      const int rr = r < 0 ? rows_lds[0] : r;
-#pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp) {
-        const uint4* p = reinterpret_cast<const uint4*>(A[sp] + (size_t)rr * lda + g * 128) + 2 * scp;
-        stg[sp][mb][0] = p[0];
-        stg[sp][mb][1] = p[1];
-      }
-    }
-  };
-  auto stage_store = [&](int buf, int g, bool sums) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      float part = 0.f;
-#pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp) {
-        const uint4 v0 = stg[sp][mb][0], v1 = stg[sp][mb][1];
-        uint4* d = a_lds + ((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16) * 32;
-        d[(2 * scp) * 32 + (srow ^ (2 * scp))] = v0;   // rows swizzled by chunk pair: the 16
-        d[(2 * scp + 1) * 32 + (srow ^ (2 * scp))] = v1;   // lanes of one store cycle hit 16 bank groups
-        part += bf16x8_sum(v0) + bf16x8_sum(v1);
-      }
-      part += dpp_f32<DPP_XOR1>(part);   // the 8 threads of one row
-      part += dpp_f32<DPP_XOR2>(part);
-      part += dpp_f32<DPP_HALF_MIRROR>(part);
-      if (sums && scp == 0) rsum_lds[(mb * 32 + srow) * KG + g] = part;
-    }
-  };
+// chunk c of tile row r of part sp at a[sp][c][r]: the 32 rows of one chunk
+// are one contiguous 512-byte run (a conflict-free fragment read, at a fixed
+// offset from the lane's base address), and the one-slot pad per chunk puts
+// the 16 chunks of a row that one staging store writes in distinct banks
+template <int K, int NSPLIT>
+struct PrTile {
+  uint4 a[NSPLIT][K / 8][PR_TM + 1];
+  float rsum[PR_TM][K / G];
+  int rows[PR_TM];   // source row of each tile row; -1: padding (reads row 0, never stored)
+};
 
-  // One K-group: codes of group g in `cur`; the codes of group g + 2 are
-  // loaded into `nxt2` and the A tile of g + 1 into registers, then stored
-  // to the other LDS buffer after the MFMAs.
-  auto group = [&](int g, Codes& cur, Codes& nxt2) {
-    const int buf = g & 1;
-    stage_load(min(g + 1, KG - 1));
-    load_codes(min(g + 2, KG - 1), nxt2);
-    // keep the loads ahead of the MFMAs, and their first uses (the stores of
-    // the next A tile) after them
-    __builtin_amdgcn_sched_barrier(0);
-    pf_f32x16 temp[NMAT][NB][2];
+// Stage the tile whose source rows are in T.rows: thread (row tid / 16, chunk
+// lane tid % 16) loads chunks 16 g + lane of every group g and part; the 16
+// lanes of a row then sum each group (R) with DPP.
+template <int K, int NSPLIT>
+__device__ __forceinline__ void pr_stage_load(const uint16_t* const (&A)[NSPLIT], const PrTile<K, NSPLIT>& T,
+                                              uint4 (&v)[NSPLIT][K / G]) {
+  constexpr int KG = K / G;
+  static_assert(NSPLIT * KG == 16 && PR_NT == PR_TM * 16, "16 loads per thread");
+  const int r = threadIdx.x >> 4, cl = threadIdx.x & 15;
+  const int src = T.rows[r] < 0 ? T.rows[0] : T.rows[r];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 8 * hl + j;   // chunk of the group
-      uint4 af[NSPLIT][2];
+  for (int sp = 0; sp < NSPLIT; ++sp)
 #pragma unroll
-      for (int sp = 0; sp < NSPLIT; ++sp)
+    for (int g = 0; g < KG; ++g) v[sp][g] = reinterpret_cast<const uint4*>(A[sp] + (size_t)src * K)[16 * g + cl];
+}
+
+template <int K, int NSPLIT>
+__device__ __forceinline__ void pr_stage_store(PrTile<K, NSPLIT>& T, const uint4 (&v)[NSPLIT][K / G]) {
+  constexpr int KG = K / G;
+  const int r = threadIdx.x >> 4, cl = threadIdx.x & 15;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          af[sp][mb] = a_lds[((size_t)((buf * NSPLIT + sp) * 2 + mb) * 16 + c) * 32 + (lrow ^ (c & 14))];
+  for (int g = 0; g < KG; ++g) {
+    float part = 0.f;
 #pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
+    for (int sp = 0; sp < NSPLIT; ++sp) {
+      const int c = 16 * g + cl;
+      T.a[sp][c][r] = v[sp][g];
+      part += bf16x8_sum(v[sp][g]);
+    }
+    part += dpp_f32<DPP_XOR1>(part);   // the 16 chunks of the group
+    part += dpp_f32<DPP_XOR2>(part);
+    part += dpp_f32<DPP_HALF_MIRROR>(part);
+    part += dpp_f32<DPP_MIRROR>(part);
+    if (cl == 0) T.rsum[r][g] = part;
+  }
+}
+
+// codes and scale bits of one step (K-group) for this lane's row of each matrix
+template <int NMAT>
+struct PrStep {
+  uint4 c[NMAT][2];
+  uint32_t s[NMAT];
+};
+
+// W and S in the tile-major layout (one contiguous 1 KB load per half step
+// and matrix, one 64-byte run of scales)
+template <int K, int NMAT>
+__device__ __forceinline__ void pr_load(const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT], int row,
+                                        int g, PrStep<NMAT>& d) {
+  constexpr int KG = K / G;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint4 cw = cur.c[mat][nb][j >> 2];
+  for (int mat = 0; mat < NMAT; ++mat) {
+    const uint4* p = reinterpret_cast<const uint4*>(W[mat] + (size_t)(row >> 5) * (32 * K / 2)) + g * 128 + lane;
+    d.c[mat][0] = p[0];
+    d.c[mat][1] = p[64];
+    d.s[mat] = S[mat][(size_t)(row >> 5) * (32 * KG) + g * 32 + (row & 31)];
+  }
+}
+
+// The first PR_D steps of a wave's stream (issued before the tile is staged).
+template <int K, int NMAT>
+__device__ __forceinline__ void pr_prologue(const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT],
+                                            int wrow0, PrStep<NMAT> (&ring)[PR_D]) {
+#pragma unroll
+  for (int u = 0; u < PR_D; ++u) pr_load<K, NMAT>(W, S, wrow0 + (threadIdx.x & 31), u, ring[u]);
+}
+
+// The wave's NB blocks of 32 weight rows (wrow0 + 32 nb + lane % 32) against
+// the staged tile; epi(nb, acc) receives each block's results: register r of
+// acc[mat] is tile row 8 (r / 4) + 4 hl + r % 4, weight row wrow0 + 32 nb + lane % 32.
+template <int K, int NSPLIT, int NMAT, int NB, class Epi>
+__device__ __forceinline__ void pr_compute(const PrTile<K, NSPLIT>& T, const uint8_t* const (&W)[NMAT],
+                                           const uint16_t* const (&S)[NMAT], int wrow0, PrStep<NMAT> (&ring)[PR_D],
+                                           Epi epi) {
+  constexpr int KG = K / G;
+  static_assert(KG % PR_D == 0 && KG <= 16, "ring steps per group count");
+  const int lane = threadIdx.x & 63, lrow = lane & 31, hl = lane >> 5;
+  // R of this lane's tile row, groups 8 hl .. 8 hl + 7, in three bf16 parts
+  uint4 rp[3];
+  {
+    uint32_t w3[3][4] = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = 8 * hl + i;
+      const float v = g < KG ? T.rsum[lrow][g] : 0.f;
+      const uint32_t b0 = f32_to_bf16_rne(v);
+      const float r1 = v - bf16_bits_to_f32(b0);
+      const uint32_t b1 = f32_to_bf16_rne(r1);
+      const uint32_t b2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1));
+      const int sh = 16 * (i & 1);
+      w3[0][i >> 1] |= b0 << sh;
+      w3[1][i >> 1] |= b1 << sh;
+      w3[2][i >> 1] |= b2 << sh;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) rp[k] = make_uint4(w3[k][0], w3[k][1], w3[k][2], w3[k][3]);
+  }
+  // A fragments of MFMA step q = 8 g + j, read PR_FA steps before their use
+  constexpr int PR_FA = 2;
+  auto frag = [&](int q, uint4 (&d)[NSPLIT]) {
+    const int c = 16 * (q >> 3) + 8 * hl + (q & 7);
+#pragma unroll
+    for (int sp = 0; sp < NSPLIT; ++sp) d[sp] = T.a[sp][c][lrow];
+  };
+#pragma unroll 1
+  for (int nb = 0; nb < NB; ++nb) {
+    pf_f32x16 acc[NMAT];
+    uint32_t sw[NMAT][4] = {};   // scales of groups 8 hl .. 8 hl + 7 for the correction
+    const int row_next = wrow0 + 32 * min(nb + 1, NB - 1) + lrow;
+    uint4 fr[PR_FA + 1][NSPLIT];
+#pragma unroll
+    for (int q = 0; q < PR_FA; ++q) frag(q, fr[q]);
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      PrStep<NMAT>& cur = ring[g % PR_D];
+      pf_f32x16 tmp[NMAT];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = 8 * g + j;
+        if (q + PR_FA < 8 * KG) frag(q + PR_FA, fr[(q + PR_FA) % (PR_FA + 1)]);
+        const uint4 (&af)[NSPLIT] = fr[q % (PR_FA + 1)];
+#pragma unroll
+        for (int mat = 0; mat < NMAT; ++mat) {
+          const uint4 cw = cur.c[mat][j >> 2];
           const uint32_t dw = (j & 3) == 0 ? cw.x : (j & 3) == 1 ? cw.y : (j & 3) == 2 ? cw.z : cw.w;
           const uint4 bx = expand_codes(dw);
 #pragma unroll
           for (int sp = 0; sp < NSPLIT; ++sp)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-              temp[mat][nb][mb] = mfma_bf16(af[sp][mb], bx, (j == 0 && sp == 0) ? pf_f32x16{} : temp[mat][nb][mb]);
+            tmp[mat] = mfma_bf16(af[sp], bx, (j == 0 && sp == 0) ? pf_f32x16{} : tmp[mat]);
         }
+      }
+#pragma unroll
+      for (int mat = 0; mat < NMAT; ++mat) {
+        const uint32_t sb = cur.s[mat] & 0xFFFFu;
+        const float sc = bf16_bits_to_f32(sb);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[mat][r] = g == 0 ? sc * tmp[mat][r] : fmaf(sc, tmp[mat][r], acc[mat][r]);
+          // computed here: sunk into the epilogue's stores, it would keep
+          // every group's partial sums alive until then
+          asm volatile("" : "+v"(acc[mat][r]));
+        }
+        if ((g >> 3) == hl) sw[mat][(g & 7) >> 1] |= sb << (16 * (g & 1));
+      }
+      // refill this ring slot with the step PR_D ahead (the next block's
+      // first groups; past the last block, its last rows again, unused)
+      if (g + PR_D < KG)
+        pr_load<K, NMAT>(W, S, wrow0 + 32 * nb + lrow, g + PR_D, cur);
+      else
+        pr_load<K, NMAT>(W, S, row_next, g + PR_D - KG, cur);
+      // one step at a time: nothing of the next step is hoisted into this one
+      // (its fragment reads and expansions would hold registers the ring needs)
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
+    for (int mat = 0; mat < NMAT; ++mat) {
+      const uint4 sb = make_uint4(sw[mat][0], sw[mat][1], sw[mat][2], sw[mat][3]);
+      pf_f32x16 corr = mfma_bf16(rp[0], sb, pf_f32x16{});
+      corr = mfma_bf16(rp[1], sb, corr);
+      corr = mfma_bf16(rp[2], sb, corr);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const float sc = bf16_bits_to_f32(cur.s[mat][nb]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(sc, temp[mat][nb][mb][r], acc[mat][nb][mb][r]);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    stage_store(buf ^ 1, g + 1, g + 1 < KG);   // after the last group: unused
-    wg_sync();
-  };
-
-  // Codes run two groups ahead of the MFMAs (three register sets, rotated
-  // after each group), the A tile one group ahead.
-  Codes c0, c1, c2;
-  load_codes(0, c0);
-  load_codes(min(1, KG - 1), c1);
-  stage_load(0);
-  stage_store(0, 0, true);
-  wg_sync();
-#pragma unroll 1
-  for (int g = 0; g < KG; ++g) {
-    group(g, c0, c2);
-    c0 = c1;
-    c1 = c2;
+      for (int r = 0; r < 16; ++r) acc[mat][r] = fmaf(-136.f, corr[r], acc[mat][r]);
+    }
+    epi(nb, acc);
   }
-
-  // -136 sum_g s[n][g] R[m][g]: K = the KG groups (zero-padded to 16)
-  uint4 rp[3][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    uint32_t h2[4], m2[4], l2[4];
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      float v[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int g = 8 * hl + i + u;
-        v[u] = g < KG ? rsum_lds[(mb * 32 + lrow) * KG + g] : 0.f;
-      }
-      uint32_t hb[2], mbits[2], lb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        hb[u] = f32_to_bf16_rne(v[u]);
-        const float r1 = v[u] - bf16_bits_to_f32(hb[u]);
-        mbits[u] = f32_to_bf16_rne(r1);
-        lb[u] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mbits[u]));
-      }
-      h2[i / 2] = hb[0] | (hb[1] << 16);
-      m2[i / 2] = mbits[0] | (mbits[1] << 16);
-      l2[i / 2] = lb[0] | (lb[1] << 16);
-    }
-    rp[0][mb] = make_uint4(h2[0], h2[1], h2[2], h2[3]);
-    rp[1][mb] = make_uint4(m2[0], m2[1], m2[2], m2[3]);
-    rp[2][mb] = make_uint4(l2[0], l2[1], l2[2], l2[3]);
-  }
-#pragma unroll
-  for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint16_t* sp = S[mat] + (size_t)(wrow0 + nb * 32 + lrow) * KG;
-      uint32_t sw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const int g = 8 * hl + i;
-        if (g + 1 < KG) sw[i / 2] = (uint32_t)sp[g] | ((uint32_t)sp[g + 1] << 16);
-      }
-      const uint4 sb = make_uint4(sw[0], sw[1], sw[2], sw[3]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        pf_f32x16 corr = mfma_bf16(rp[0][mb], sb, pf_f32x16{});
-        corr = mfma_bf16(rp[1][mb], sb, corr);
-        corr = mfma_bf16(rp[2][mb], sb, corr);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mat][nb][mb][r] = fmaf(-136.f, corr[r], acc[mat][nb][mb][r]);
-      }
-    }
 }
 
-// tile row of accumulator register r of row block mb
-__device__ __forceinline__ int tile_row(int mb, int r) {
-  return mb * 32 + 8 * (r >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (r & 3);
-}
+// tile row of accumulator register r
+__device__ __forceinline__ int pr_row(int r) { return 8 * (r >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (r & 3); }
 
 // h = silu(g) u as bf16 hi + lo at pair-order position of feature col
 __device__ __forceinline__ void store_h(uint16_t* hi_row, uint16_t* lo_row, int col, float g, float u) {
@@ -476,12 +484,9 @@ __device__ __forceinline__ void store_h(uint16_t* hi_row, uint16_t* lo_row, int 
   lo_row[p] = (uint16_t)lo;
 }
 
-constexpr int LDS_A1 = 2 * 1 * 2 * 16 * 32;   // uint4, NSPLIT = 1
-constexpr int LDS_A2 = 2 * 2 * 2 * 16 * 32;   // uint4, NSPLIT = 2
-
-// Work items of the persistent GEMM kernels: (tile, N-slice) pairs, numbered
-// so that the NT slices of one tile are 8 apart (one XCD, whose L2 then holds
-// the tile's A rows) and come up in the same round of the grid.
+// Work items of the dense (shared-expert) kernels: (tile, N-slice) pairs,
+// numbered so that the NT slices of one tile are 8 apart (one XCD, whose L2
+// then holds the tile's A rows) and come up in the same round of the grid.
 __device__ __forceinline__ void pf_item(int q, int nt_count, int& tile, int& nt) {
   tile = 8 * (q / (8 * nt_count)) + (q & 7);
   nt = (q >> 3) % nt_count;
@@ -489,83 +494,89 @@ __device__ __forceinline__ void pf_item(int q, int nt_count, int& tile, int& nt)
 __host__ __device__ constexpr int pf_items(int tiles, int nt_count) { return (tiles + 7) / 8 * 8 * nt_count; }
 
 // ------------------------------------------------------------- routed gate/up
-__global__ void __launch_bounds__(PF_NT, 2) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
-                                                      const int* __restrict__ tile_start, const int* __restrict__ perm,
-                                                      LayerW L, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A1];
-  __shared__ __align__(16) float rsum[PF_TM * (H / G)];
-  __shared__ int rows[PF_TM];
-  constexpr int NT = I / 128;
+// Item: one tile (<= 32 (token, slot) pairs of one expert) against all 512
+// gate and 512 up rows; wave w takes rows 64 w .. 64 w + 63 of both.  The
+// workgroups of XCD x (blockIdx % 8) walk the tiles dealt to x.
+__global__ void __launch_bounds__(PR_NT) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
+                                                     const int* __restrict__ tile_start, const int* __restrict__ perm,
+                                                     LayerW P, uint16_t* __restrict__ h_hi,
+                                                     uint16_t* __restrict__ h_lo) {
+  __shared__ PrTile<H, 1> T;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  // this XCD's tiles, the NT column slices of a tile on consecutive workgroups
-  const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * NT;
-  for (int q = blockIdx.x >> 3; q < items; q += gridDim.x >> 3) {
-    const int nt = q % NT;
-    const int4 tl = tiles[t0 + q / NT];
+  const int x = blockIdx.x & 7, t0 = tile_start[x], ntl = tile_start[x + 1] - t0;
+  const int wrow0 = wave * 64;
+  const uint16_t* const Ap[1] = {a};
+  for (int q = blockIdx.x >> 3; q < ntl; q += gridDim.x >> 3) {
+    const int4 tl = tiles[t0 + q];
     const int e = tl.x, pos0 = tl.y, cnt = tl.z;
-    wg_sync();   // the previous item is done with the LDS
-    if (tid < PF_TM) rows[tid] = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
+    const uint8_t* const W[2] = {P.gate + (size_t)e * I * (H / 2), P.up + (size_t)e * I * (H / 2)};
+    const uint16_t* const S[2] = {P.gate_s + (size_t)e * I * (H / G), P.up_s + (size_t)e * I * (H / G)};
+    const int pr = tid < cnt ? perm[pos0 + tid] / TOPK : -1;
+    wg_sync();   // the previous item is done with the tile
+    if (tid < PR_TM) T.rows[tid] = pr;
     wg_sync();
-    const int wrow0 = nt * 128 + wave * 32;
-    const uint8_t* const W[2] = {L.gate + (size_t)e * I * (H / 2), L.up + (size_t)e * I * (H / 2)};
-    const uint16_t* const S[2] = {L.gate_s + (size_t)e * I * (H / G), L.up_s + (size_t)e * I * (H / G)};
-    const uint16_t* const Ap[1] = {a};
-    pf_f32x16 acc[2][1][2] = {};
-    gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, rsum);
-    const int col = wrow0 + lrow;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    uint4 v[1][H / G];
+    pr_stage_load<H, 1>(Ap, T, v);
+    PrStep<2> ring[PR_D];
+    pr_prologue<H, 2>(W, S, wrow0, ring);
+    pr_stage_store<H, 1>(T, v);
+    wg_sync();
+    pr_compute<H, 1, 2, 2>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
+      const int col = wrow0 + 32 * nb + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tile_row(mb, r);
-        if (m < cnt) store_h(h_hi + (size_t)(pos0 + m) * I, h_lo + (size_t)(pos0 + m) * I, col, acc[0][0][mb][r],
-                             acc[1][0][mb][r]);
+        const int m = pr_row(r);
+        if (m < cnt) store_h(h_hi + (size_t)(pos0 + m) * I, h_lo + (size_t)(pos0 + m) * I, col, acc[0][r], acc[1][r]);
       }
+    });
   }
 }
 
 // ------------------------------------------------------------- shared gate/up
-__global__ void __launch_bounds__(PF_NT, 2) k_pf_sh_gateup(const uint16_t* __restrict__ a, int n, LayerW L,
-                                                         uint16_t* __restrict__ hs_hi, uint16_t* __restrict__ hs_lo) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A1];
-  __shared__ __align__(16) float rsum[PF_TM * (H / G)];
-  __shared__ int rows[PF_TM];
-  constexpr int NT = IS / 128;
-  const int T = (n + PF_TM - 1) / PF_TM;
+// Item: 32 consecutive tokens against a quarter of the shared gate and up rows
+// (256 each); wave w takes rows 32 w .. 32 w + 31 of the quarter.
+constexpr int PS_NQ = IS / 256;
+__global__ void __launch_bounds__(PR_NT) k_pf_sh_gateup(const uint16_t* __restrict__ a, int n, LayerW P,
+                                                        uint16_t* __restrict__ hs_hi, uint16_t* __restrict__ hs_lo) {
+  __shared__ PrTile<H, 1> T;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
-    int ti, nt;
-    pf_item(q, NT, ti, nt);
-    if (ti >= T) continue;
-    const int m0 = ti * PF_TM;
+  const int nt = (n + PR_TM - 1) / PR_TM;
+  const uint8_t* const W[2] = {P.sh_gate, P.sh_up};
+  const uint16_t* const S[2] = {P.sh_gate_s, P.sh_up_s};
+  const uint16_t* const Ap[1] = {a};
+  for (int q = blockIdx.x; q < pf_items(nt, PS_NQ); q += gridDim.x) {
+    int ti, nq;
+    pf_item(q, PS_NQ, ti, nq);
+    if (ti >= nt) continue;
+    const int m0 = ti * PR_TM, wrow0 = nq * 256 + wave * 32;
     wg_sync();
-    if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+    if (tid < PR_TM) T.rows[tid] = m0 + tid < n ? m0 + tid : -1;
     wg_sync();
-    const int wrow0 = nt * 128 + wave * 32;
-    const uint8_t* const W[2] = {L.sh_gate, L.sh_up};
-    const uint16_t* const S[2] = {L.sh_gate_s, L.sh_up_s};
-    const uint16_t* const Ap[1] = {a};
-    pf_f32x16 acc[2][1][2] = {};
-    gemm_tile<1, 2, H / G, 1>(Ap, H, rows, W, S, wrow0, acc, a_lds, rsum);
-    const int col = wrow0 + lrow;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    uint4 v[1][H / G];
+    pr_stage_load<H, 1>(Ap, T, v);
+    PrStep<2> ring[PR_D];
+    pr_prologue<H, 2>(W, S, wrow0, ring);
+    pr_stage_store<H, 1>(T, v);
+    wg_sync();
+    pr_compute<H, 1, 2, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
+      const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + tile_row(mb, r);
-        if (m < n) store_h(hs_hi + (size_t)m * IS, hs_lo + (size_t)m * IS, col, acc[0][0][mb][r], acc[1][0][mb][r]);
+        const int t = m0 + pr_row(r);
+        if (t < n) store_h(hs_hi + (size_t)t * IS, hs_lo + (size_t)t * IS, col, acc[0][r], acc[1][r]);
       }
+    });
   }
 }
 
 // ------------------------------------------------------------- routed down
-// Work item: 32 rows of a tile (a half tile) x a quarter of the H output
-// columns.  The half tile's h rows (both bf16 parts, all of K = 512: 64 KB)
-// are staged into LDS once; each wave then streams the int4 rows of its 128
-// columns in blocks of 32, the codes of the next block in flight during the
-// MFMAs of the current one.  Output: y[pair][col] for each (token, slot) pair.
-constexpr int PD_TM = 32;              // rows of a half tile
-constexpr int PD_NQ = 4;               // column quarters of H per half tile
+// Work item: a tile (<= 32 (token, slot) pairs of one expert) x a quarter of
+// the H output columns.  The tile's h rows (both bf16 parts, all of K = 512:
+// 64 KB) are staged into LDS once; each wave then streams the int4 rows of its
+// 128 columns in blocks of 32, the codes of the next block in flight during
+// the MFMAs of the current one.  Output: y[pair][col] for each (token, slot) pair.
+constexpr int PD_TM = PF_TM;           // rows of a tile
+constexpr int PD_NQ = 4;               // column quarters of H per tile
 constexpr int PD_NB = H / PD_NQ / 128; // 32-column blocks per wave (4 waves)
 constexpr int PD_KC = I / 8;           // 8-element chunks of a row (64)
 constexpr int PD_KG = I / G;           // K-groups (4)
@@ -577,17 +588,20 @@ struct DownCodes {
   uint2 s;   // the row's 4 bf16 scales
 };
 
+// W, S in the tile-major layout (prefill.h): 32 rows x all of K = 8 KB
 __device__ __forceinline__ void down_load(const uint8_t* W, const uint16_t* S, int row, int hl, DownCodes& d) {
-  const uint4* p = reinterpret_cast<const uint4*>(W + (size_t)row * (I / 2)) + 2 * hl;
+  const int lane = threadIdx.x & 63;
+  const uint4* p = reinterpret_cast<const uint4*>(W + (size_t)(row >> 5) * (32 * I / 2)) + lane;
 #pragma unroll
   for (int g = 0; g < PD_KG; ++g) {
-    d.c[g][0] = p[4 * g];
-    d.c[g][1] = p[4 * g + 1];
+    d.c[g][0] = p[128 * g];
+    d.c[g][1] = p[128 * g + 64];
   }
-  d.s = *reinterpret_cast<const uint2*>(S + (size_t)row * PD_KG);
+  const uint16_t* sp = S + (size_t)(row >> 5) * (32 * PD_KG) + (row & 31);
+  d.s = make_uint2((uint32_t)sp[0] | ((uint32_t)sp[32] << 16), (uint32_t)sp[64] | ((uint32_t)sp[96] << 16));
 }
 
-// One 32 x 32 output block: rows of the half tile, columns of code block d.
+// One 32 x 32 output block: rows of the tile, columns of code block d.
 // a_lds[part][chunk][slot]: chunk c of tile row r at slot r ^ (c & 15).
 __device__ __forceinline__ pf_f32x16 down_block(const uint4 (*a_lds)[PD_KC][PD_TM], const DownCodes& d,
                                                 const uint4 (&rp)[3], int lrow, int hl) {
@@ -624,23 +638,22 @@ __device__ __forceinline__ pf_f32x16 down_block(const uint4 (*a_lds)[PD_KC][PD_T
 __global__ void __launch_bounds__(PF_NT, 2) k_pf_down(const uint16_t* __restrict__ h_hi,
                                                        const uint16_t* __restrict__ h_lo,
                                                        const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-                                                       const int* __restrict__ perm, LayerW L, float* __restrict__ y) {
+                                                       const int* __restrict__ perm, LayerW P, float* __restrict__ y) {
   __shared__ __align__(16) uint4 a_lds[2][PD_KC][PD_TM];
   __shared__ float rsum[PD_TM][PD_KG];
   __shared__ int pairs[PD_TM];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
-  // this XCD's half tiles, the column quarters of one on consecutive workgroups
-  const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * 2 * PD_NQ;
+  // this XCD's tiles, the column quarters of one on consecutive workgroups
+  const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * PD_NQ;
   for (int q = blockIdx.x >> 3; q < items; q += gridDim.x >> 3) {
-    const int ht = q / PD_NQ, nq = q % PD_NQ;
-    const int4 tl = tiles[t0 + (ht >> 1)];
-    const int e = tl.x, pos = tl.y + PD_TM * (ht & 1), rows = min(tl.z - PD_TM * (ht & 1), PD_TM);
-    if (rows <= 0) continue;
-    const uint8_t* W = L.down + (size_t)e * H * (I / 2);
-    const uint16_t* S = L.down_s + (size_t)e * H * PD_KG;
+    const int nq = q % PD_NQ;
+    const int4 tl = tiles[t0 + q / PD_NQ];
+    const int e = tl.x, pos = tl.y, rows = tl.z;
+    const uint8_t* W = P.down + (size_t)e * H * (I / 2);
+    const uint16_t* S = P.down_s + (size_t)e * H * PD_KG;
     const int n0 = nq * (H / PD_NQ) + wave * (PD_NB * 32);
     wg_sync();   // the previous item is done with the LDS
-    // stage the half tile: thread = (chunk lane, rows wave + 4 i); padding rows
+    // stage the tile: thread = (chunk lane, rows wave + 4 i); padding rows
     // read the first row
     uint4 st[8][2];
 #pragma unroll
@@ -691,7 +704,7 @@ __global__ void __launch_bounds__(PF_NT, 2) k_pf_down(const uint16_t* __restrict
       const int col = n0 + nb * 32 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = tile_row(0, r);
+        const int m = pr_row(r);
         if (m < rows) y[(size_t)pairs[m] * H + col] = acc[r];
       }
     };
@@ -714,50 +727,99 @@ __global__ void __launch_bounds__(PF_NT, 2) k_pf_down(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------- shared down + combine
-__global__ void __launch_bounds__(PF_NT) k_pf_sh_down(const float* xin, float* out, int n,
-                                                       const uint16_t* __restrict__ hs_hi,
-                                                       const uint16_t* __restrict__ hs_lo, LayerW L,
-                                                       const float* __restrict__ w, const float* __restrict__ y) {
-  __shared__ __align__(16) uint4 a_lds[LDS_A2];
-  __shared__ __align__(16) float rsum[PF_TM * (IS / G)];
-  __shared__ int rows[PF_TM];
-  constexpr int NT = H / 256;
-  const int T = (n + PF_TM - 1) / PF_TM;
+// Item: 32 consecutive tokens against an eighth of the output columns (256);
+// wave w takes columns 32 w .. 32 w + 31 of it.  The epilogue adds the routed
+// outputs in slot order and the residual: out = x + ((w0 y0 + w1 y1) + ... + w5 y5) + y_shared.
+constexpr int PS_NS = H / 256;
+__global__ void __launch_bounds__(PR_NT) k_pf_sh_down(const float* xin, float* out, int n,
+                                                      const uint16_t* __restrict__ hs_hi,
+                                                      const uint16_t* __restrict__ hs_lo, LayerW P,
+                                                      const float* __restrict__ w, const float* __restrict__ y) {
+  __shared__ PrTile<IS, 2> T;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
-  for (int q = blockIdx.x; q < pf_items(T, NT); q += gridDim.x) {
-    int ti, nt;
-    pf_item(q, NT, ti, nt);
-    if (ti >= T) continue;
-    const int m0 = ti * PF_TM;
+  const int nt = (n + PR_TM - 1) / PR_TM;
+  const uint8_t* const W[1] = {P.sh_down};
+  const uint16_t* const S[1] = {P.sh_down_s};
+  const uint16_t* const Ap[2] = {hs_hi, hs_lo};
+  for (int q = blockIdx.x; q < pf_items(nt, PS_NS); q += gridDim.x) {
+    int ti, ns;
+    pf_item(q, PS_NS, ti, ns);
+    if (ti >= nt) continue;
+    const int m0 = ti * PR_TM, wrow0 = ns * 256 + wave * 32;
     wg_sync();
-    if (tid < PF_TM) rows[tid] = m0 + tid < n ? m0 + tid : -1;
+    if (tid < PR_TM) T.rows[tid] = m0 + tid < n ? m0 + tid : -1;
     wg_sync();
-    const int wrow0 = nt * 256 + wave * 64;
-    const uint8_t* const W[1] = {L.sh_down};
-    const uint16_t* const S[1] = {L.sh_down_s};
-    const uint16_t* const Ap[2] = {hs_hi, hs_lo};
-    pf_f32x16 acc[1][2][2] = {};
-    gemm_tile<2, 1, IS / G, 2>(Ap, IS, rows, W, S, wrow0, acc, a_lds, rsum);
+    uint4 v[2][IS / G];
+    pr_stage_load<IS, 2>(Ap, T, v);
+    PrStep<1> ring[PR_D];
+    pr_prologue<IS, 1>(W, S, wrow0, ring);
+    pr_stage_store<IS, 2>(T, v);
+    wg_sync();
+    pr_compute<IS, 2, 1, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
+      const int col = wrow0 + lrow;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int col = wrow0 + nb * 32 + lrow;
+      for (int r = 0; r < 16; ++r) {
+        const int t = m0 + pr_row(r);
+        if (t < n) {
+          const float* wt = w + (size_t)t * TOPK;
+          const float* yt = y + (size_t)t * TOPK * H + col;
+          float d = wt[0] * yt[0];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = m0 + tile_row(mb, r);
-          if (t < n) {
-            const float* wt = w + (size_t)t * TOPK;
-            const float* yt = y + (size_t)t * TOPK * H + col;
-            float d = wt[0] * yt[0];
-#pragma unroll
-            for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
-            d += acc[0][nb][mb][r];
-            out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
-          }
+          for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
+          d += acc[0][r];
+          out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
         }
-    }
+      }
+    });
   }
+}
+
+// ------------------------------------------------------------- tile-major copy
+// Codes: one thread per 16-byte piece of the destination; rows of kb bytes.
+__global__ void k_pf_pack_codes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, size_t rows, int kb) {
+  const int kg = kb / 64;
+  const size_t total = rows * kb / 16;
+  for (size_t o = blockIdx.x * (size_t)blockDim.x + threadIdx.x; o < total; o += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(o & 63), i = (int)((o >> 6) & 1);
+    const size_t bg = o >> 7;   // (row block, group)
+    const int g = (int)(bg % kg);
+    const size_t row = 32 * (bg / kg) + (lane & 31);
+    reinterpret_cast<uint4*>(dst)[o] =
+        *reinterpret_cast<const uint4*>(src + row * kb + 64 * g + 32 * (lane >> 5) + 16 * i);
+  }
+}
+
+// Scales: [rows][kg] -> [rows / 32][kg][32].
+__global__ void k_pf_pack_scales(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, size_t rows, int kg) {
+  const size_t total = rows * kg;
+  for (size_t o = blockIdx.x * (size_t)blockDim.x + threadIdx.x; o < total; o += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = o & 31, bg = o >> 5;
+    dst[o] = src[(32 * (bg / kg) + r) * kg + bg % kg];
+  }
+}
+
+hipError_t prefill_pack_layer(const LayerW& src, const LayerW& dst, hipStream_t s) {
+  struct M {
+    const uint8_t* c;
+    const uint16_t* sc;
+    const uint8_t* pc;
+    const uint16_t* ps;
+    size_t rows;
+    int k;
+  };
+  const M ms[6] = {{src.gate, src.gate_s, dst.gate, dst.gate_s, (size_t)E * I, H},
+                   {src.up, src.up_s, dst.up, dst.up_s, (size_t)E * I, H},
+                   {src.down, src.down_s, dst.down, dst.down_s, (size_t)E * H, I},
+                   {src.sh_gate, src.sh_gate_s, dst.sh_gate, dst.sh_gate_s, (size_t)IS, H},
+                   {src.sh_up, src.sh_up_s, dst.sh_up, dst.sh_up_s, (size_t)IS, H},
+                   {src.sh_down, src.sh_down_s, dst.sh_down, dst.sh_down_s, (size_t)H, IS}};
+  for (const M& m : ms) {
+    hipLaunchKernelGGL(k_pf_pack_codes, dim3(4096), dim3(256), 0, s, m.c, const_cast<uint8_t*>(m.pc), m.rows,
+                       m.k / 2);
+    hipLaunchKernelGGL(k_pf_pack_scales, dim3(1024), dim3(256), 0, s, m.sc, const_cast<uint16_t*>(m.ps), m.rows,
+                       m.k / G);
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- host side
@@ -784,10 +846,10 @@ int prefill_workspace_alloc(PrefillWS* ws, char** mem, alloc_fn alloc) {
   return FLINT_OK;
 }
 
-hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const PrefillWS& ws,
-                                int* trace_ids, float* trace_w, hipStream_t s) {
+hipError_t launch_prefill_layer(const float* xin, float* out, int n, const LayerW& L, const LayerW& P,
+                                const PrefillWS& ws, int* trace_ids, float* trace_w, hipStream_t s) {
   if (n <= DECODE_MAX_TOKENS || n > FLINT_MAX_TOKENS) return hipErrorInvalidValue;
-  const int mt = (n + PF_TM - 1) / PF_TM;
+  const int mt = (n + PR_TM - 1) / PR_TM;
   hipLaunchKernelGGL(k_pf_input, dim3(n), dim3(PF_NT), 0, s, xin, n, ws.a, ws.bitmap);
   hipLaunchKernelGGL(k_pf_router, dim3((n + 31) / 32, E / 32), dim3(PF_NT), 0, s, ws.a, n, L.router, ws.z);
   hipLaunchKernelGGL(k_pf_route, dim3((n + 3) / 4), dim3(PF_NT), 0, s, ws.z, n, L.bias, ws.ids, ws.w, ws.bitmap,
@@ -795,17 +857,19 @@ hipError_t launch_prefill_layer(const float* xin, float* out, int n, const Layer
   hipLaunchKernelGGL(k_pf_offsets, dim3(1), dim3(E), 0, s, ws.bitmap, n, ws.offsets, ws.tiles, ws.tile_start);
   hipLaunchKernelGGL(k_pf_scatter, dim3((n * TOPK + PF_NT - 1) / PF_NT), dim3(PF_NT), 0, s, ws.ids, n, ws.bitmap,
                      ws.offsets, ws.perm);
-  // persistent grids: about one round of resident workgroups, at most one per item
+  // persistent grids: at most one round of resident workgroups (one per CU
+  // for the resident-tile kernels, whose tile fills most of the LDS), at most
+  // one per item; the routed kernels' grids are multiples of 8 (one XCD's
+  // workgroups walk that XCD's tiles)
   auto grid = [](int items, int resident) { return dim3(std::max(1, std::min(items, resident))); };
-  // routed GEMMs: two resident workgroups per CU, 64 per XCD (a multiple of 8)
-  hipLaunchKernelGGL(k_pf_gateup, dim3(2 * 256), dim3(PF_NT), 0, s, ws.a, ws.tiles, ws.tile_start, ws.perm, L,
-                     ws.h_hi, ws.h_lo);
-  hipLaunchKernelGGL(k_pf_sh_gateup, grid(pf_items(mt, IS / 128), 2 * 256), dim3(PF_NT), 0, s, ws.a, n, L, ws.hs_hi,
+  hipLaunchKernelGGL(k_pf_gateup, dim3(256), dim3(PR_NT), 0, s, ws.a, ws.tiles, ws.tile_start, ws.perm, P, ws.h_hi,
+                     ws.h_lo);
+  hipLaunchKernelGGL(k_pf_sh_gateup, grid(pf_items(mt, PS_NQ), 256), dim3(PR_NT), 0, s, ws.a, n, P, ws.hs_hi,
                      ws.hs_lo);
   hipLaunchKernelGGL(k_pf_down, dim3(2 * 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles, ws.tile_start, ws.perm,
-                     L, ws.y);
-  hipLaunchKernelGGL(k_pf_sh_down, grid(pf_items(mt, H / 256), 256), dim3(PF_NT), 0, s, xin, out, n, ws.hs_hi,
-                     ws.hs_lo, L, ws.w, ws.y);
+                     P, ws.y);
+  hipLaunchKernelGGL(k_pf_sh_down, grid(pf_items(mt, PS_NS), 256), dim3(PR_NT), 0, s, xin, out, n, ws.hs_hi,
+                     ws.hs_lo, P, ws.w, ws.y);
   return hipGetLastError();
 }
 

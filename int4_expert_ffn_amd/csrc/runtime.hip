@@ -46,9 +46,16 @@ struct LayerSizes {
   size_t sh_down = (size_t)H * (IS / 2), sh_down_s = (size_t)H * (IS / G) * 2;
   size_t list[14] = {router, bias, gate, gate_s, gate, gate_s, down, down_s,
                      sh_gu, sh_gu_s, sh_gu, sh_gu_s, sh_down, sh_down_s};
-  size_t total() const {
+  // the row-major tensors, then the tile-major copies of tensors 2..13 (the
+  // int4 matrices and their scales) that the prefill path streams
+  size_t row_major() const {
     size_t t = 0;
     for (size_t s : list) t += align_up(s);
+    return t;
+  }
+  size_t total() const {
+    size_t t = row_major();
+    for (int i = 2; i < 14; ++i) t += align_up(list[i]);
     return t;
   }
 };
@@ -60,6 +67,7 @@ struct flint_moe {
   int n_layers = 0;
   char* arena = nullptr;
   std::vector<LayerW> layers;
+  std::vector<LayerW> players;   // tile-major copies of the int4 matrices (prefill)
   DecodeWS dws{};
   char* dws_mem = nullptr;
   PrefillWS pws{};
@@ -156,6 +164,7 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
   int rc = checked_malloc((void**)&h->arena, per_layer * n_layers, "weights");
   if (rc) { release(h); return rc; }
   h->layers.resize(n_layers);
+  h->players.resize(n_layers);
   h->layer_stride = per_layer;
   for (int l = 0; l < n_layers; ++l) {
     const flint_moe_layer& w = weights[l];
@@ -186,6 +195,27 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
     L.sh_up_s = (const uint16_t*)dst[11];
     L.sh_down = (const uint8_t*)dst[12];
     L.sh_down_s = (const uint16_t*)dst[13];
+    char* pk[14] = {};
+    for (int i = 2; i < 14; ++i) {
+      pk[i] = base + off;
+      off += align_up(sz.list[i]);
+    }
+    LayerW& P = h->players[l];
+    P = L;
+    P.gate = (const uint8_t*)pk[2];
+    P.gate_s = (const uint16_t*)pk[3];
+    P.up = (const uint8_t*)pk[4];
+    P.up_s = (const uint16_t*)pk[5];
+    P.down = (const uint8_t*)pk[6];
+    P.down_s = (const uint16_t*)pk[7];
+    P.sh_gate = (const uint8_t*)pk[8];
+    P.sh_gate_s = (const uint16_t*)pk[9];
+    P.sh_up = (const uint8_t*)pk[10];
+    P.sh_up_s = (const uint16_t*)pk[11];
+    P.sh_down = (const uint8_t*)pk[12];
+    P.sh_down_s = (const uint16_t*)pk[13];
+    e = prefill_pack_layer(L, P, nullptr);
+    if (e != hipSuccess) { rc = fail_hip(e, "packing weights"); release(h); return rc; }
   }
   // decode workspace
   {
@@ -302,7 +332,7 @@ int flint_moe_forward(flint_moe_t h, const float* x, int n_tokens, int layer_beg
     if (n_tokens <= DECODE_MAX_TOKENS)
       e = launch_decode_layer(xin, out, n_tokens, h->layers[l], h->dws, tid, tw, s);
     else
-      e = launch_prefill_layer(xin, out, n_tokens, h->layers[l], h->pws, tid, tw, s);
+      e = launch_prefill_layer(xin, out, n_tokens, h->layers[l], h->players[l], h->pws, tid, tw, s);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
   }
   return FLINT_OK;
