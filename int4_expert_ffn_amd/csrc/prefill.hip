@@ -310,7 +310,7 @@ template <int K, int NSPLIT>
 __device__ __forceinline__ void pr_stage_load(const uint16_t* const (&A)[NSPLIT], const PrTile<K, NSPLIT>& T,
                                               uint4 (&v)[NSPLIT][K / G]) {
   constexpr int KG = K / G;
-  static_assert(NSPLIT * KG == 16 && PR_NT == PR_TM * 16, "16 loads per thread");
+  static_assert(NSPLIT * KG <= 16 && PR_NT == PR_TM * 16, "at most 16 loads per thread");
   const int r = threadIdx.x >> 4, cl = threadIdx.x & 15;
   const int src = T.rows[r] < 0 ? T.rows[0] : T.rows[r];
 #pragma unroll
@@ -474,9 +474,15 @@ __device__ __forceinline__ void pr_compute(const PrTile<K, NSPLIT>& T, const uin
 // tile row of accumulator register r
 __device__ __forceinline__ int pr_row(int r) { return 8 * (r >> 2) + 4 * ((threadIdx.x >> 5) & 1) + (r & 3); }
 
+// silu(g) u with the hardware exponential and reciprocal (each within a few
+// fp32 ulps; the prefill bound on the block output is 2e-5)
+__device__ __forceinline__ float pf_silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 // h = silu(g) u as bf16 hi + lo at pair-order position of feature col
 __device__ __forceinline__ void store_h(uint16_t* hi_row, uint16_t* lo_row, int col, float g, float u) {
-  const float hv = silu_mul(g, u);
+  const float hv = pf_silu_mul(g, u);
   const uint32_t hi = f32_to_bf16_rne(hv);
   const uint32_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
   const int p = perm_order(col);
@@ -494,9 +500,12 @@ __device__ __forceinline__ void pf_item(int q, int nt_count, int& tile, int& nt)
 __host__ __device__ constexpr int pf_items(int tiles, int nt_count) { return (tiles + 7) / 8 * 8 * nt_count; }
 
 // ------------------------------------------------------------- routed gate/up
-// Item: one tile (<= 32 (token, slot) pairs of one expert) against all 512
-// gate and 512 up rows; wave w takes rows 64 w .. 64 w + 63 of both.  The
-// workgroups of XCD x (blockIdx % 8) walk the tiles dealt to x.
+// Item: one tile (<= 32 (token, slot) pairs of one expert) against half of the
+// gate and up rows (256 each); wave w takes rows 32 w .. 32 w + 31 of the
+// half.  The workgroups of XCD x (blockIdx % 8) walk the items of the tiles
+// dealt to x; both halves of a tile run there, so its A rows and the expert's
+// weights are shared through that XCD's L2.  (Whole tiles per item would
+// leave some CUs a third round: about 520 tiles for 256 CUs at 2,048 tokens.)
 __global__ void __launch_bounds__(PR_NT) k_pf_gateup(const uint16_t* __restrict__ a, const int4* __restrict__ tiles,
                                                      const int* __restrict__ tile_start, const int* __restrict__ perm,
                                                      LayerW P, uint16_t* __restrict__ h_hi,
@@ -504,10 +513,10 @@ __global__ void __launch_bounds__(PR_NT) k_pf_gateup(const uint16_t* __restrict_
   __shared__ PrTile<H, 1> T;
   const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
   const int x = blockIdx.x & 7, t0 = tile_start[x], ntl = tile_start[x + 1] - t0;
-  const int wrow0 = wave * 64;
   const uint16_t* const Ap[1] = {a};
-  for (int q = blockIdx.x >> 3; q < ntl; q += gridDim.x >> 3) {
-    const int4 tl = tiles[t0 + q];
+  for (int q = blockIdx.x >> 3; q < 2 * ntl; q += gridDim.x >> 3) {
+    const int4 tl = tiles[t0 + (q >> 1)];
+    const int wrow0 = (q & 1) * (I / 2) + wave * 32;
     const int e = tl.x, pos0 = tl.y, cnt = tl.z;
     const uint8_t* const W[2] = {P.gate + (size_t)e * I * (H / 2), P.up + (size_t)e * I * (H / 2)};
     const uint16_t* const S[2] = {P.gate_s + (size_t)e * I * (H / G), P.up_s + (size_t)e * I * (H / G)};
@@ -521,8 +530,8 @@ __global__ void __launch_bounds__(PR_NT) k_pf_gateup(const uint16_t* __restrict_
     pr_prologue<H, 2>(W, S, wrow0, ring);
     pr_stage_store<H, 1>(T, v);
     wg_sync();
-    pr_compute<H, 1, 2, 2>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
-      const int col = wrow0 + 32 * nb + lrow;
+    pr_compute<H, 1, 2, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
+      const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = pr_row(r);
@@ -570,159 +579,49 @@ __global__ void __launch_bounds__(PR_NT) k_pf_sh_gateup(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------- routed down
-// Work item: a tile (<= 32 (token, slot) pairs of one expert) x a quarter of
-// the H output columns.  The tile's h rows (both bf16 parts, all of K = 512:
-// 64 KB) are staged into LDS once; each wave then streams the int4 rows of its
-// 128 columns in blocks of 32, the codes of the next block in flight during
-// the MFMAs of the current one.  Output: y[pair][col] for each (token, slot) pair.
-constexpr int PD_TM = PF_TM;           // rows of a tile
-constexpr int PD_NQ = 4;               // column quarters of H per tile
-constexpr int PD_NB = H / PD_NQ / 128; // 32-column blocks per wave (4 waves)
-constexpr int PD_KC = I / 8;           // 8-element chunks of a row (64)
-constexpr int PD_KG = I / G;           // K-groups (4)
-static_assert(PD_KC == 64 && PD_KG == 4 && PD_NB == 4, "routed down layout");
-
-// codes and scales of one lane's weight row: group g, bytes 32 hl + [0, 32)
-struct DownCodes {
-  uint4 c[PD_KG][2];
-  uint2 s;   // the row's 4 bf16 scales
-};
-
-// W, S in the tile-major layout (prefill.h): 32 rows x all of K = 8 KB
-__device__ __forceinline__ void down_load(const uint8_t* W, const uint16_t* S, int row, int hl, DownCodes& d) {
-  const int lane = threadIdx.x & 63;
-  const uint4* p = reinterpret_cast<const uint4*>(W + (size_t)(row >> 5) * (32 * I / 2)) + lane;
-#pragma unroll
-  for (int g = 0; g < PD_KG; ++g) {
-    d.c[g][0] = p[128 * g];
-    d.c[g][1] = p[128 * g + 64];
-  }
-  const uint16_t* sp = S + (size_t)(row >> 5) * (32 * PD_KG) + (row & 31);
-  d.s = make_uint2((uint32_t)sp[0] | ((uint32_t)sp[32] << 16), (uint32_t)sp[64] | ((uint32_t)sp[96] << 16));
-}
-
-// One 32 x 32 output block: rows of the tile, columns of code block d.
-// a_lds[part][chunk][slot]: chunk c of tile row r at slot r ^ (c & 15).
-__device__ __forceinline__ pf_f32x16 down_block(const uint4 (*a_lds)[PD_KC][PD_TM], const DownCodes& d,
-                                                const uint4 (&rp)[3], int lrow, int hl) {
-  pf_f32x16 acc;
-#pragma unroll
-  for (int g = 0; g < PD_KG; ++g) {
-    pf_f32x16 temp;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 16 * g + 8 * hl + j;
-      const uint4 a0 = a_lds[0][c][lrow ^ (8 * hl + j)];
-      const uint4 a1 = a_lds[1][c][lrow ^ (8 * hl + j)];
-      const uint4 cw = d.c[g][j >> 2];
-      const uint32_t dw = (j & 3) == 0 ? cw.x : (j & 3) == 1 ? cw.y : (j & 3) == 2 ? cw.z : cw.w;
-      const uint4 bx = expand_codes(dw);
-      temp = mfma_bf16(a0, bx, j == 0 ? pf_f32x16{} : temp);
-      temp = mfma_bf16(a1, bx, temp);
-    }
-    const uint32_t sbits = (g & 1) ? ((g < 2 ? d.s.x : d.s.y) >> 16) : ((g < 2 ? d.s.x : d.s.y) & 0xFFFFu);
-    const float sc = bf16_bits_to_f32(sbits);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = g == 0 ? sc * temp[r] : fmaf(sc, temp[r], acc[r]);
-  }
-  // -136 sum_g s[n][g] R[m][g]: K = the 4 groups in lanes 0..31, zero-padded
-  const uint4 sb = hl == 0 ? make_uint4(d.s.x, d.s.y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
-  pf_f32x16 corr = mfma_bf16(rp[0], sb, pf_f32x16{});
-  corr = mfma_bf16(rp[1], sb, corr);
-  corr = mfma_bf16(rp[2], sb, corr);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = fmaf(-136.f, corr[r], acc[r]);
-  return acc;
-}
-
-__global__ void __launch_bounds__(PF_NT, 2) k_pf_down(const uint16_t* __restrict__ h_hi,
-                                                       const uint16_t* __restrict__ h_lo,
-                                                       const int4* __restrict__ tiles, const int* __restrict__ tile_start,
-                                                       const int* __restrict__ perm, LayerW P, float* __restrict__ y) {
-  __shared__ __align__(16) uint4 a_lds[2][PD_KC][PD_TM];
-  __shared__ float rsum[PD_TM][PD_KG];
-  __shared__ int pairs[PD_TM];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lrow = lane & 31, hl = lane >> 5;
-  // this XCD's tiles, the column quarters of one on consecutive workgroups
+// Item: a tile (<= 32 (token, slot) pairs of one expert) x a quarter of the H
+// output columns (512); wave w takes columns 64 w .. 64 w + 63 of it.  A is
+// the tile's h (both bf16 parts, K = 512: 64 KB of LDS, so two workgroups
+// share a CU: four waves per SIMD, 128 registers).  Output: y[pair][col]
+// for each (token, slot) pair.
+constexpr int PD_NQ = 4;   // column quarters of H per tile
+__global__ void __launch_bounds__(PR_NT, 4) k_pf_down(const uint16_t* __restrict__ h_hi,
+                                                      const uint16_t* __restrict__ h_lo,
+                                                      const int4* __restrict__ tiles, const int* __restrict__ tile_start,
+                                                      const int* __restrict__ perm, LayerW P, float* __restrict__ y) {
+  __shared__ PrTile<I, 2> T;
+  __shared__ int pairs[PR_TM];
+  const int tid = threadIdx.x, wave = tid >> 6, lrow = tid & 31;
+  // this XCD's tiles, the column quarters of one on consecutive items
   const int x = blockIdx.x & 7, t0 = tile_start[x], items = (tile_start[x + 1] - t0) * PD_NQ;
+  const uint16_t* const Ap[2] = {h_hi, h_lo};
   for (int q = blockIdx.x >> 3; q < items; q += gridDim.x >> 3) {
-    const int nq = q % PD_NQ;
     const int4 tl = tiles[t0 + q / PD_NQ];
-    const int e = tl.x, pos = tl.y, rows = tl.z;
-    const uint8_t* W = P.down + (size_t)e * H * (I / 2);
-    const uint16_t* S = P.down_s + (size_t)e * H * PD_KG;
-    const int n0 = nq * (H / PD_NQ) + wave * (PD_NB * 32);
-    wg_sync();   // the previous item is done with the LDS
-    // stage the tile: thread = (chunk lane, rows wave + 4 i); padding rows
-    // read the first row
-    uint4 st[8][2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave + 4 * i;
-      const size_t src = (size_t)(pos + (r < rows ? r : 0)) * I;
-      st[i][0] = reinterpret_cast<const uint4*>(h_hi + src)[lane];
-      st[i][1] = reinterpret_cast<const uint4*>(h_lo + src)[lane];
-    }
-    const int pr = tid < rows ? perm[pos + tid] : 0;
-    DownCodes c0, c1;
-    down_load(W, S, n0 + lrow, hl, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (tid < PD_TM) pairs[tid] = pr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = wave + 4 * i;
-      a_lds[0][lane][r ^ (lane & 15)] = st[i][0];
-      a_lds[1][lane][r ^ (lane & 15)] = st[i][1];
-      float part = bf16x8_sum(st[i][0]) + bf16x8_sum(st[i][1]);
-      part += dpp_f32<DPP_XOR1>(part);   // the 16 chunks of one group
-      part += dpp_f32<DPP_XOR2>(part);
-      part += dpp_f32<DPP_HALF_MIRROR>(part);
-      part += dpp_f32<DPP_MIRROR>(part);
-      if ((lane & 15) == 0) rsum[r][lane >> 4] = part;
+    const int e = tl.x, pos0 = tl.y, cnt = tl.z;
+    const int wrow0 = (q % PD_NQ) * (H / PD_NQ) + wave * 64;
+    const uint8_t* const W[1] = {P.down + (size_t)e * H * (I / 2)};
+    const uint16_t* const S[1] = {P.down_s + (size_t)e * H * (I / G)};
+    const int pr = tid < cnt ? perm[pos0 + tid] : 0;
+    wg_sync();   // the previous item is done with the tile
+    if (tid < PR_TM) {
+      T.rows[tid] = tid < cnt ? pos0 + tid : -1;
+      pairs[tid] = pr;
     }
     wg_sync();
-    // R of this lane's row split into three bf16 parts (exact products)
-    uint4 rp[3];
-    {
-      uint32_t w3[3][2] = {};
-#pragma unroll
-      for (int g = 0; g < PD_KG; ++g) {
-        const float v = hl == 0 ? rsum[lrow][g] : 0.f;
-        const uint32_t b0 = f32_to_bf16_rne(v);
-        const float r1 = v - bf16_bits_to_f32(b0);
-        const uint32_t b1 = f32_to_bf16_rne(r1);
-        const uint32_t b2 = f32_to_bf16_rne(r1 - bf16_bits_to_f32(b1));
-        const int sh = 16 * (g & 1);
-        w3[0][g >> 1] |= b0 << sh;
-        w3[1][g >> 1] |= b1 << sh;
-        w3[2][g >> 1] |= b2 << sh;
-      }
-#pragma unroll
-      for (int k = 0; k < 3; ++k) rp[k] = make_uint4(w3[k][0], w3[k][1], 0u, 0u);
-    }
-    auto store = [&](int nb, const pf_f32x16& acc) {
-      const int col = n0 + nb * 32 + lrow;
+    uint4 v[2][I / G];
+    pr_stage_load<I, 2>(Ap, T, v);
+    PrStep<1> ring[PR_D];
+    pr_prologue<I, 1>(W, S, wrow0, ring);
+    pr_stage_store<I, 2>(T, v);
+    wg_sync();
+    pr_compute<I, 2, 1, 2>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
+      const int col = wrow0 + 32 * nb + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = pr_row(r);
-        if (m < rows) y[(size_t)pairs[m] * H + col] = acc[r];
+        if (m < cnt) y[(size_t)pairs[m] * H + col] = acc[0][r];
       }
-    };
-    // four column blocks, two code sets in turn (no register copies while a
-    // load is in flight)
-    down_load(W, S, n0 + 32 + lrow, hl, c1);
-    __builtin_amdgcn_sched_barrier(0);
-    store(0, down_block(a_lds, c0, rp, lrow, hl));
-    __builtin_amdgcn_sched_barrier(0);
-    down_load(W, S, n0 + 64 + lrow, hl, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    store(1, down_block(a_lds, c1, rp, lrow, hl));
-    __builtin_amdgcn_sched_barrier(0);
-    down_load(W, S, n0 + 96 + lrow, hl, c1);
-    __builtin_amdgcn_sched_barrier(0);
-    store(2, down_block(a_lds, c0, rp, lrow, hl));
-    __builtin_amdgcn_sched_barrier(0);
-    store(3, down_block(a_lds, c1, rp, lrow, hl));
+    });
   }
 }
 
@@ -866,7 +765,7 @@ hipError_t launch_prefill_layer(const float* xin, float* out, int n, const Layer
                      ws.h_lo);
   hipLaunchKernelGGL(k_pf_sh_gateup, grid(pf_items(mt, PS_NQ), 256), dim3(PR_NT), 0, s, ws.a, n, P, ws.hs_hi,
                      ws.hs_lo);
-  hipLaunchKernelGGL(k_pf_down, dim3(2 * 256), dim3(PF_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles, ws.tile_start, ws.perm,
+  hipLaunchKernelGGL(k_pf_down, dim3(2 * 256), dim3(PR_NT), 0, s, ws.h_hi, ws.h_lo, ws.tiles, ws.tile_start, ws.perm,
                      P, ws.y);
   hipLaunchKernelGGL(k_pf_sh_down, grid(pf_items(mt, PS_NS), 256), dim3(PR_NT), 0, s, xin, out, n, ws.hs_hi,
                      ws.hs_lo, P, ws.w, ws.y);
