@@ -272,8 +272,8 @@ __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ id
 // One workgroup of PR_NT threads (8 waves) computes a tile of 32 A rows against
 // weight rows.  The whole tile, all of K, sits in LDS for the item, so the K
 // loop needs no barrier: each wave streams the int4 codes and scales of its
-// own weight rows through a ring of PR_D register sets (step = one K-group of
-// 32 rows of each weight matrix), the loads of step s + PR_D in flight while
+// own weight rows through a ring of RD register sets (step = one K-group of
+// 32 rows of each weight matrix), the loads of step s + RD in flight while
 // step s runs on the matrix cores.
 //
 // A: bf16 rows of K elements in pair-order 8-element chunks, NSPLIT parts
@@ -290,7 +290,8 @@ __global__ void __launch_bounds__(PF_NT) k_pf_scatter(const int* __restrict__ id
 // that its products are exact.
 constexpr int PR_TM = 32;    // A rows of a tile
 constexpr int PR_NT = 512;   // threads of the resident-tile kernels (8 waves)
-constexpr int PR_D = 2;      // steps of weight loads in flight per wave
+constexpr int PR_D = 2;      // steps of weight loads in flight per wave (4 measured slower: more requests
+                             // in flight congest the memory system rather than hide its latency)
 
 // chunk c of tile row r of part sp at a[sp][c][r]: the 32 rows of one chunk
 // are one contiguous 512-byte run (a conflict-free fragment read, at a fixed
@@ -363,23 +364,23 @@ __device__ __forceinline__ void pr_load(const uint8_t* const (&W)[NMAT], const u
   }
 }
 
-// The first PR_D steps of a wave's stream (issued before the tile is staged).
-template <int K, int NMAT>
+// The first RD steps of a wave's stream (issued before the tile is staged).
+template <int K, int NMAT, int RD>
 __device__ __forceinline__ void pr_prologue(const uint8_t* const (&W)[NMAT], const uint16_t* const (&S)[NMAT],
-                                            int wrow0, PrStep<NMAT> (&ring)[PR_D]) {
+                                            int wrow0, PrStep<NMAT> (&ring)[RD]) {
 #pragma unroll
-  for (int u = 0; u < PR_D; ++u) pr_load<K, NMAT>(W, S, wrow0 + (threadIdx.x & 31), u, ring[u]);
+  for (int u = 0; u < RD; ++u) pr_load<K, NMAT>(W, S, wrow0 + (threadIdx.x & 31), u, ring[u]);
 }
 
 // The wave's NB blocks of 32 weight rows (wrow0 + 32 nb + lane % 32) against
 // the staged tile; epi(nb, acc) receives each block's results: register r of
 // acc[mat] is tile row 8 (r / 4) + 4 hl + r % 4, weight row wrow0 + 32 nb + lane % 32.
-template <int K, int NSPLIT, int NMAT, int NB, class Epi>
+template <int K, int NSPLIT, int NMAT, int NB, int RD, class Epi>
 __device__ __forceinline__ void pr_compute(const PrTile<K, NSPLIT>& T, const uint8_t* const (&W)[NMAT],
-                                           const uint16_t* const (&S)[NMAT], int wrow0, PrStep<NMAT> (&ring)[PR_D],
+                                           const uint16_t* const (&S)[NMAT], int wrow0, PrStep<NMAT> (&ring)[RD],
                                            Epi epi) {
   constexpr int KG = K / G;
-  static_assert(KG % PR_D == 0 && KG <= 16, "ring steps per group count");
+  static_assert(KG % RD == 0 && KG <= 16, "ring steps per group count");
   const int lane = threadIdx.x & 63, lrow = lane & 31, hl = lane >> 5;
   // R of this lane's tile row, groups 8 hl .. 8 hl + 7, in three bf16 parts
   uint4 rp[3];
@@ -418,7 +419,7 @@ __device__ __forceinline__ void pr_compute(const PrTile<K, NSPLIT>& T, const uin
     for (int q = 0; q < PR_FA; ++q) frag(q, fr[q]);
 #pragma unroll
     for (int g = 0; g < KG; ++g) {
-      PrStep<NMAT>& cur = ring[g % PR_D];
+      PrStep<NMAT>& cur = ring[g % RD];
       pf_f32x16 tmp[NMAT];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -448,12 +449,12 @@ __device__ __forceinline__ void pr_compute(const PrTile<K, NSPLIT>& T, const uin
         }
         if ((g >> 3) == hl) sw[mat][(g & 7) >> 1] |= sb << (16 * (g & 1));
       }
-      // refill this ring slot with the step PR_D ahead (the next block's
+      // refill this ring slot with the step RD ahead (the next block's
       // first groups; past the last block, its last rows again, unused)
-      if (g + PR_D < KG)
-        pr_load<K, NMAT>(W, S, wrow0 + 32 * nb + lrow, g + PR_D, cur);
+      if (g + RD < KG)
+        pr_load<K, NMAT>(W, S, wrow0 + 32 * nb + lrow, g + RD, cur);
       else
-        pr_load<K, NMAT>(W, S, row_next, g + PR_D - KG, cur);
+        pr_load<K, NMAT>(W, S, row_next, g + RD - KG, cur);
       // one step at a time: nothing of the next step is hoisted into this one
       // (its fragment reads and expansions would hold registers the ring needs)
       __builtin_amdgcn_sched_barrier(0);
@@ -527,10 +528,10 @@ __global__ void __launch_bounds__(PR_NT) k_pf_gateup(const uint16_t* __restrict_
     uint4 v[1][H / G];
     pr_stage_load<H, 1>(Ap, T, v);
     PrStep<2> ring[PR_D];
-    pr_prologue<H, 2>(W, S, wrow0, ring);
+    pr_prologue<H, 2, PR_D>(W, S, wrow0, ring);
     pr_stage_store<H, 1>(T, v);
     wg_sync();
-    pr_compute<H, 1, 2, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
+    pr_compute<H, 1, 2, 1, PR_D>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
       const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -564,10 +565,10 @@ __global__ void __launch_bounds__(PR_NT) k_pf_sh_gateup(const uint16_t* __restri
     uint4 v[1][H / G];
     pr_stage_load<H, 1>(Ap, T, v);
     PrStep<2> ring[PR_D];
-    pr_prologue<H, 2>(W, S, wrow0, ring);
+    pr_prologue<H, 2, PR_D>(W, S, wrow0, ring);
     pr_stage_store<H, 1>(T, v);
     wg_sync();
-    pr_compute<H, 1, 2, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
+    pr_compute<H, 1, 2, 1, PR_D>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[2]) {
       const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -610,11 +611,11 @@ __global__ void __launch_bounds__(PR_NT, 4) k_pf_down(const uint16_t* __restrict
     wg_sync();
     uint4 v[2][I / G];
     pr_stage_load<I, 2>(Ap, T, v);
-    PrStep<1> ring[PR_D];
-    pr_prologue<I, 1>(W, S, wrow0, ring);
+    PrStep<1> ring[2];   // depth 2: four waves per SIMD leave 128 registers
+    pr_prologue<I, 1, 2>(W, S, wrow0, ring);
     pr_stage_store<I, 2>(T, v);
     wg_sync();
-    pr_compute<I, 2, 1, 2>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
+    pr_compute<I, 2, 1, 2, 2>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
       const int col = wrow0 + 32 * nb + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -651,10 +652,10 @@ __global__ void __launch_bounds__(PR_NT) k_pf_sh_down(const float* xin, float* o
     uint4 v[2][IS / G];
     pr_stage_load<IS, 2>(Ap, T, v);
     PrStep<1> ring[PR_D];
-    pr_prologue<IS, 1>(W, S, wrow0, ring);
+    pr_prologue<IS, 1, PR_D>(W, S, wrow0, ring);
     pr_stage_store<IS, 2>(T, v);
     wg_sync();
-    pr_compute<IS, 2, 1, 1>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
+    pr_compute<IS, 2, 1, 1, PR_D>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
       const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
