@@ -87,6 +87,9 @@ typedef struct {
 /* Create a handle holding n_layers layers (1 <= n_layers <= FLINT_MAX_LAYERS)
  * on the current HIP device.  Synchronous: the weights are copied into memory
  * the library owns, so the caller may free its buffers when the call returns.
+ * Besides the copy as given, the library keeps a second copy of every int4
+ * matrix and its scales rearranged for the prefill GEMMs (same size), so a
+ * handle holds about twice the weight bytes (about 0.84 GB per layer).
  * `weights` is a host array of n_layers descriptors of device pointers.
  * On failure *out is set to NULL and nothing is leaked.  Test hook: with the
  * environment variable FLINT_MOE_FAIL_ALLOC=k (k >= 1), the k-th device
