@@ -305,8 +305,10 @@ __device__ __forceinline__ void wave_block_input(const float4 (&xv)[8], const fl
 }
 
 // Gate/up: h[t][r] = silu(Wg[r] . a_t) * (Wu[r] . a_t).  Workgroup b owns rows
-// 16 b .. 16 b + 15; wave w takes K-groups 2 w and 2 w + 1 of both matrices
-// (lane l: row l % 16, the 32 elements 32 (l / 16) .. + 31 of each group).
+// rpw b .. rpw b + rpw - 1 (rpw <= 16 rows: inter / 512, so that the grid is
+// two workgroups per CU); wave w takes K-groups 2 w and 2 w + 1 of both
+// matrices (lane l: row min(l % 16, rpw - 1), the 32 elements 32 (l / 16) .. + 31
+// of each group; the MFMA columns past rpw repeat the last row and are not stored).
 // Its codes are requested before the block inputs are formed (wave w forms
 // tokens w and w + 8); the 8 waves' partial sums are added in wave order.
 struct DenseGateUpLds {
@@ -321,11 +323,11 @@ __global__ void __launch_bounds__(NT, 4) k_dense_gateup(const float* __restrict_
                                                         const uint8_t* __restrict__ gate,
                                                         const uint16_t* __restrict__ gate_s,
                                                         const uint8_t* __restrict__ up,
-                                                        const uint16_t* __restrict__ up_s, int rows,
+                                                        const uint16_t* __restrict__ up_s, int rows, int rpw,
                                                         float* __restrict__ h) {
   __shared__ DenseGateUpLds L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, q = lane >> 4;
-  const size_t row = (size_t)blockIdx.x * 16 + col;
+  const size_t row = (size_t)blockIdx.x * rpw + min(col, rpw - 1);
   // this wave's first token (w, or n - 1 when w >= n) before the codes: the
   // norm then waits for its own loads only (loads complete in issue order)
   float4 xv[8];
@@ -397,7 +399,7 @@ __global__ void __launch_bounds__(NT, 4) k_dense_gateup(const float* __restrict_
   wg_sync();
   if (threadIdx.x < 256) {
     const int c = threadIdx.x & 15, t = threadIdx.x >> 4;
-    if (t < n) {
+    if (t < n && c < rpw) {
       const int l = 16 * (t >> 2) + c, r = t & 3;
       float gsum = 0.f, usum = 0.f;
 #pragma unroll
@@ -405,13 +407,14 @@ __global__ void __launch_bounds__(NT, 4) k_dense_gateup(const float* __restrict_
         gsum += reinterpret_cast<const float*>(&L.red[v][0][l])[r];
         usum += reinterpret_cast<const float*>(&L.red[v][1][l])[r];
       }
-      h[(size_t)t * rows + (size_t)blockIdx.x * 16 + c] = silu_mul(gsum, usum);
+      h[(size_t)t * rows + (size_t)blockIdx.x * rpw + c] = silu_mul(gsum, usum);
     }
   }
 }
 
 // Down: out[t][c] = x[t][c] + Wd[c] . h_t, K = inter = 128 NG.  Workgroup b
-// owns rows 16 b .. 16 b + 15; wave w takes the K-groups w, w + 8, w + 16, ...
+// owns rows 8 b .. 8 b + 7 (256 workgroups, one per CU; the MFMA's columns
+// 8 .. 15 repeat rows 0 .. 7 and are not stored); wave w takes the K-groups w, w + 8, w + 16, ...
 // in that order, whatever the call's size, so every token's arithmetic is the
 // same for any n.  h is fp32: the workgroup splits the h values of the call's
 // tokens into three bf16 parts (v = p0 + p1 + p2 exactly: each part takes the
@@ -442,6 +445,7 @@ struct DenseDownLds {
   float R[TC][CH / 16];         // per K-group of the slice: sum of the token's h
 };
 
+constexpr int DD_RPW = 8;   // output rows per down workgroup
 template <int NG, int NI>   // K-groups (inter / 128); (token, chunk) pairs per thread and group-slice column
 __global__ void __launch_bounds__(NT, 1) k_dense_down(const float* __restrict__ h, int n,
                                                       const uint8_t* __restrict__ down,
@@ -457,7 +461,7 @@ __global__ void __launch_bounds__(NT, 1) k_dense_down(const float* __restrict__ 
   static_assert(TC * CH == NT * IT, "pairs per slice");
   __shared__ DenseDownLds<TC, CH> L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, q = lane >> 4;
-  const size_t row = (size_t)blockIdx.x * 16 + col;
+  const size_t row = (size_t)blockIdx.x * DD_RPW + (col & (DD_RPW - 1));
   // codes and scale of this wave's K-groups w + 8 k, k < NG / 8
   constexpr int KW = NG / 8;
   uint4 code[KW];
@@ -542,8 +546,8 @@ __global__ void __launch_bounds__(NT, 1) k_dense_down(const float* __restrict__ 
   }
   float xo = 0.f;
   const int oc = threadIdx.x & 15, ot = threadIdx.x >> 4;
-  const bool writer = threadIdx.x < 256 && ot < n;
-  const size_t o = (size_t)ot * H + (size_t)blockIdx.x * 16 + oc;
+  const bool writer = threadIdx.x < 256 && ot < n && oc < DD_RPW;
+  const size_t o = (size_t)ot * H + (size_t)blockIdx.x * DD_RPW + oc;
   if (writer) xo = x[o];
 #pragma unroll
   for (int tg = 0; tg < NI; ++tg) L.red[w][tg][lane] = acc[tg];
@@ -560,7 +564,7 @@ __global__ void __launch_bounds__(NT, 1) k_dense_down(const float* __restrict__ 
 template <int NG>
 static void launch_dense_down(int n, const float* h, const uint8_t* down, const uint16_t* down_s, const float* x,
                               float* out, hipStream_t s) {
-  const dim3 grid(H / 16), block(NT);
+  const dim3 grid(H / DD_RPW), block(NT);
   switch ((n + 3) / 4) {
     case 1: hipLaunchKernelGGL((k_dense_down<NG, 1>), grid, block, 0, s, h, n, down, down_s, x, out); break;
     case 2: hipLaunchKernelGGL((k_dense_down<NG, 2>), grid, block, 0, s, h, n, down, down_s, x, out); break;
@@ -577,7 +581,8 @@ hipError_t launch_dense_mlp(const uint8_t* gate, const uint16_t* gate_s, const u
                             float* out, hipStream_t s) {
   if (n < 1 || n > DENSE_MAX_TOKENS || inter < 2048 || inter > FLINT_DENSE_MLP_SIZE || inter % 2048)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_dense_gateup, dim3(inter / 16), dim3(NT), 0, s, x, n, gate, gate_s, up, up_s, inter, h);
+  const int rpw = inter / 512;   // 4, 8 or 12 rows: 512 workgroups, two per CU
+  hipLaunchKernelGGL(k_dense_gateup, dim3(inter / rpw), dim3(NT), 0, s, x, n, gate, gate_s, up, up_s, inter, rpw, h);
   if (inter == 2048)
     launch_dense_down<16>(n, h, down, down_s, x, out, s);
   else if (inter == 4096)
