@@ -361,7 +361,7 @@ def flint_stack(seed: int = 0, n_layers: int = N_LAYERS_FLINT, mult: int = 4096,
 # ---------------------------------------------------------------- decode attention
 # Attention of one layer (TandemLLM "21 Flint", 21.1 table rows "attention",
 # "sliding layers", "full layers"; How to Run Flint Locally, "Sinks and the
-# 513-token window"): 32 query heads, 4 KV heads of 128, a 513-position window
+# 513-token window"): query heads 32, KV heads 4, head size 128, a 513-position window
 # held in a ring of 640 rows on window layers, every position on full layers,
 # one learned sink logit per query head (the checkpoint's offsets run from -9.0
 # to 12.4).

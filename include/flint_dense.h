@@ -4,7 +4,8 @@
  * output head.
  *
  * The pages give their shapes (How to Run Flint Locally, "The architecture,
- * from config.json": table row "Dense MLP size", 6,144, layers 0 and 1 only;
+ * from config.json": table row "Dense MLP size": width 6,144, used by the first
+ * two layers;
  * table row "Vocabulary", 150,144; section "One decode step in bytes": the
  * lm_head is 150,144 x 2,048, every token reads all of it, and the research
  * system quantised it to 4 bits).  Both use the int4 format of flint_moe.h

@@ -251,9 +251,10 @@ __device__ __forceinline__ uint32_t fp16_bits(float v) {
 constexpr int PUB_WAVE = NWAVES - 1;
 constexpr int NPOLL = NT - 64;   // polling threads: waves 0 .. NWAVES-2
 
-// F16H: the fp16-intermediate form (TandemLLM "21 Flint", 21.2: packs store
-// each routed expert's up projection divided by a power of two so SwiGLU
-// outputs fit fp16; the divisor goes back in through the routing weights).
+// F16H: the fp16-intermediate form (TandemLLM "21 Flint", 21.2).  The up
+// matrices of the routed experts arrive scaled down by a power of two, which
+// keeps every SwiGLU output inside fp16's range; the combine multiplies the
+// routing weights by the same power of two.
 // Every expert's SwiGLU output is rounded to fp16; the h exchange carries two
 // values per word; routed weights are scaled by A.interm_mult in the combine.
 template <bool F16H>

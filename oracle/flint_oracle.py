@@ -209,10 +209,11 @@ def moe_block(a, src, layer: int, shape, forced=None) -> BlockResult:
 
 
 # ------------------------------------------------------------------ fp16 intermediates
-# TandemLLM "21 Flint", 21.2: SwiGLU outputs of the routed experts reach about
-# 2.6e5 in the top layers, past fp16, so the published packs store each routed
-# expert's up projection divided by a power of two (expert_interm_div, 128
-# there), with the divisor restored on the routing weights at run time.  Readings: the
+# TandemLLM "21 Flint", 21.2: in the last layers of the stack the routed
+# experts' SwiGLU outputs grow to about 2.6e5, beyond fp16's largest value.
+# The pack format therefore ships every routed up matrix scaled down by a
+# power of two (expert_interm_div, 128 on that page) and scales the routing
+# weights back up by it when the block runs.  Readings: the
 # SwiGLU output of every expert, routed and shared, is rounded to fp16 before
 # its down projection (round to nearest even, +-inf past the largest finite
 # value); only the routed up projections are divided; gate and up are as in
@@ -352,8 +353,8 @@ def bytes_per_token_layer(shape, n_tokens_experts: int = None) -> int:
 # One layer's attention for one query token (How to Run Flint Locally, "Sinks
 # and the 513-token window": a sliding layer attends over 513 positions, its own
 # and the previous 512; a sink is one more softmax slot with a fixed logit, the head's
-# learned offset, and no value vector.  TandemLLM "21 Flint", 21.1 table: 32
-# query heads, 4 KV heads of 128; window layers keep a ring of 640 rows; full
+# learned offset, and no value vector.  TandemLLM "21 Flint", 21.1 table: query
+# heads 32, KV heads 4, head size 128; window layers keep a ring of 640 rows; full
 # layers see every position).  Readings: query head h reads KV head
 # h // (32 / 4) (consecutive query heads share a KV head); scores are
 # q . k / sqrt(128); the query, keys and values arrive already normed and

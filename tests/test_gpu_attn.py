@@ -1,5 +1,5 @@
 """GPU parity of the decode attention with learned sinks against the oracle
-(TandemLLM "21 Flint", 21.1 table: 32 query heads, 4 KV heads of 128, a
+(TandemLLM "21 Flint", 21.1 table: query heads 32, KV heads 4, head size 128, a
 513-position window in a ring of 640 rows on window layers, every position on
 full layers; How to Run Flint Locally, "Sinks and the 513-token window").
 
