@@ -11,9 +11,10 @@
 //   k_pf_offsets  per-expert counts, their exclusive scan, the 32-row tiles
 //   k_pf_scatter  (token, slot) pairs in expert order, tokens increasing
 //                 within an expert (popcounts of the bitmap prefix)
-//   k_pf_gateup   routed gate/up + SwiGLU per tile (grouped GEMM)
-//   k_pf_sh_gateup  shared gate/up + SwiGLU (dense GEMM)
-//   k_pf_down     routed down projection per tile -> y by (token, slot)
+//   k_pf_gateup   routed gate/up + SwiGLU per (tile, half of the rows)
+//   k_pf_sh_gateup  shared gate/up + SwiGLU (32 tokens, a quarter of the rows)
+//   k_pf_down     routed down projection per (tile, quarter of H) -> y by
+//                 (token, slot)
 //   k_pf_sh_down  shared down projection and the fixed-order combine
 //                 out = x + ((w0 y0 + w1 y1) + ... + w5 y5) + y_shared
 //
