@@ -187,13 +187,25 @@ __device__ __forceinline__ int snake_rank(int x, int j) { return 16 * (j >> 1) +
 
 constexpr int PF_NT_BINS = FLINT_MAX_TOKENS / PF_TM + 1;   // tile counts 0..64 of one expert
 
+// Inclusive sum over the lanes of each aligned group of W lanes (W = 32 or 64).
+template <int W>
+__device__ __forceinline__ int group_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < W; d <<= 1) {
+    const int o = __shfl_up(v, d, W);
+    if ((lane & (W - 1)) >= d) v += o;
+  }
+  return v;
+}
+
 __global__ void __launch_bounds__(E) k_pf_offsets(const uint32_t* __restrict__ bitmap, int n, int* __restrict__ offsets,
                                                    int4* __restrict__ tiles, int* __restrict__ tile_start) {
-  __shared__ int sc[2][E];
-  __shared__ int nt_hist[PF_NT_BINS];
+  __shared__ int wsum[E / 64];
+  __shared__ int nt_hist[PF_NT_BINS], nt_above[PF_NT_BINS];
   __shared__ uint32_t nt_mask[PF_NT_BINS][E / 32];   // experts with a given tile count
-  __shared__ int nt_by_rank[E], xcd_tiles[8];
-  const int e = threadIdx.x;
+  __shared__ int nt_by_rank[E], dealt_before[E], xcd_tiles[8];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   for (int i = e; i < PF_NT_BINS * (E / 32); i += E) (&nt_mask[0][0])[i] = 0u;
   if (e < PF_NT_BINS) nt_hist[e] = 0;
   // the bitmap is cleared in full for every layer, so all words are read
@@ -208,32 +220,43 @@ __global__ void __launch_bounds__(E) k_pf_offsets(const uint32_t* __restrict__ b
   wg_sync();
   atomicAdd(&nt_hist[nt], 1);
   atomicOr(&nt_mask[nt][e >> 5], 1u << (e & 31));
-  int vc = cnt, b = 0;
-  for (int d = 1; d < E; d <<= 1) {   // inclusive scan (fixed shape); its barriers also order the atomics
-    sc[b][e] = vc;
-    wg_sync();
-    if (e >= d) vc += sc[b][e - d];
-    b ^= 1;
-  }
+  // inclusive scan of the counts: within each wave, then the waves' totals
+  const int vw = group_inclusive_sum<64>(cnt);
+  if (lane == 63) wsum[wave] = vw;
+  wg_sync();   // also orders the atomics above
+  int vc = vw;
+  for (int w = 0; w < wave; ++w) vc += wsum[w];
   const int oc = vc - cnt;
   offsets[e] = oc;
   if (e == E - 1) offsets[E] = vc;
+  // experts with more tiles than each count (bins above it), by one wave
+  if (wave == 0) {
+    // lane l takes bin PF_NT_BINS - 1 - l (bins 64 .. 1); bin 0 has nothing above
+    // bin 1 but is never needed above anything: nt_above[v] = sum of bins > v
+    const int bin = PF_NT_BINS - 1 - lane;   // 64 .. 1
+    const int incl = group_inclusive_sum<64>(nt_hist[bin]);
+    nt_above[bin - 1] = incl;                // bins >= bin, i.e. > bin - 1
+    if (lane == 0) nt_above[PF_NT_BINS - 1] = 0;
+  }
+  wg_sync();
   // rank: experts with more tiles first, equal counts by index
-  int r = 0;
-  for (int v = nt + 1; v < PF_NT_BINS; ++v) r += nt_hist[v];
+  int r = nt_above[nt];
   for (int w = 0; w < (e >> 5); ++w) r += __popc(nt_mask[nt][w]);
   r += __popc(nt_mask[nt][e >> 5] & ((1u << (e & 31)) - 1u));
   nt_by_rank[r] = nt;
   wg_sync();
-  const int u = r & 15, x = u < 8 ? u : 15 - u, j = r >> 3;
-  int before = 0;   // tiles of the experts dealt to XCD x ahead of this one
-  for (int jj = 0; jj < j; ++jj) before += nt_by_rank[snake_rank(x, jj)];
-  if (e < 8) {
-    int tot = 0;
-    for (int jj = 0; jj < E / 8; ++jj) tot += nt_by_rank[snake_rank(e, jj)];
-    xcd_tiles[e] = tot;
+  // dealing: thread (x, j) = (e / 32, e % 32) holds the tiles of the j-th
+  // expert dealt to XCD x; exclusive sums over j give each one's place
+  {
+    const int x = e >> 5, jj = e & 31;
+    const int v = nt_by_rank[snake_rank(x, jj)];
+    const int incl = group_inclusive_sum<32>(v);
+    dealt_before[e] = incl - v;
+    if (jj == 31) xcd_tiles[x] = incl;
   }
   wg_sync();
+  const int u = r & 15, x = u < 8 ? u : 15 - u, j = r >> 3;
+  const int before = dealt_before[32 * x + j];   // tiles of the experts dealt to XCD x ahead of this one
   int base = 0;
   for (int xx = 0; xx < x; ++xx) base += xcd_tiles[xx];
   if (e <= 8) {
