@@ -151,6 +151,13 @@ int flint_moe_status(flint_moe_t h, void* stream);
  * otherwise.  Not thread-safe with respect to calls on the same handle. */
 int flint_moe_debug_set_epoch(flint_moe_t h, uint32_t epoch);
 
+/* Testing hook.  The number of device allocations that the process's handles
+ * hold right now (each create makes 10 and destroy releases them; a failed
+ * create releases those it had made before it returns).  Device-level free
+ * memory cannot show this exactly, since the HIP runtime may keep freed blocks
+ * for reuse and hand them back to the device later.  Never fails. */
+int flint_moe_debug_live_allocations(void);
+
 /* Release the handle and its device memory.  NULL is ignored. */
 void flint_moe_destroy(flint_moe_t h);
 

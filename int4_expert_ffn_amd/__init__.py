@@ -44,7 +44,8 @@ FLINT_ATT_MAX_TOKENS = 16
 FLINT_ATT_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ("flint_moe_create", "flint_moe_create_fp16_interm", "flint_moe_forward", "flint_moe_set_trace",
-            "flint_moe_status", "flint_moe_debug_set_epoch", "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward",
+            "flint_moe_status", "flint_moe_debug_set_epoch", "flint_moe_debug_live_allocations",
+            "flint_moe_destroy", "flint_moe_last_error", "flint_dense_mlp_forward",
             "flint_head_forward", "flint_attn_workspace_bytes", "flint_attn_decode", "flint_attn_decode_noalloc")
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.flint_moe_status.restype = ci
         L.flint_moe_debug_set_epoch.argtypes = [vp, ctypes.c_uint32]
         L.flint_moe_debug_set_epoch.restype = ci
+        L.flint_moe_debug_live_allocations.argtypes = []
+        L.flint_moe_debug_live_allocations.restype = ci
         L.flint_moe_destroy.argtypes = [vp]
         L.flint_moe_destroy.restype = None
         L.flint_moe_last_error.argtypes = []
@@ -164,6 +167,10 @@ def flint_moe_status(h, stream=None) -> None:
 
 def flint_moe_debug_set_epoch(h, epoch) -> None:
     _check(lib().flint_moe_debug_set_epoch(h, epoch))
+
+
+def flint_moe_debug_live_allocations() -> int:
+    return lib().flint_moe_debug_live_allocations()
 
 
 def flint_moe_destroy(h) -> None:

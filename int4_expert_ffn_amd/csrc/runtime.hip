@@ -1,6 +1,7 @@
 // C ABI of the Flint MoE library: handle, argument validation, the
 // library-owned weight arena, workspaces, tracing and error reporting.
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -90,19 +91,29 @@ struct flint_moe {
   int interm_div = 0;       // 0: fp32 SwiGLU outputs; else the fp16-intermediate form with this divisor
 };
 
+// Device allocations held by all handles of the process (every one is made by
+// checked_malloc below and released by dev_free).
+static std::atomic<int> g_live_allocs{0};
+
+static void dev_free(void* p) {
+  if (!p) return;
+  (void)hipFree(p);
+  g_live_allocs.fetch_sub(1, std::memory_order_relaxed);
+}
+
 static void release(flint_moe* h) {
   if (!h) return;
   if (h->device >= 0) (void)hipSetDevice(h->device);
-  if (h->arena) (void)hipFree(h->arena);
-  if (h->dws_mem) (void)hipFree(h->dws_mem);
-  if (h->pws_mem) (void)hipFree(h->pws_mem);
-  if (h->dev_error) (void)hipFree(h->dev_error);
-  if (h->layers_dev) (void)hipFree(h->layers_dev);
-  if (h->xz) (void)hipFree(h->xz);
-  if (h->xh) (void)hipFree(h->xh);
-  if (h->xx) (void)hipFree(h->xx);
-  if (h->vx) (void)hipFree(h->vx);
-  if (h->vh) (void)hipFree(h->vh);
+  dev_free(h->arena);
+  dev_free(h->dws_mem);
+  dev_free(h->pws_mem);
+  dev_free(h->dev_error);
+  dev_free(h->layers_dev);
+  dev_free(h->xz);
+  dev_free(h->xh);
+  dev_free(h->xx);
+  dev_free(h->vx);
+  dev_free(h->vh);
   delete h;
 }
 
@@ -126,6 +137,7 @@ static int checked_malloc(void** p, size_t bytes, const char* what) {
       return fail(FLINT_ERR_OUT_OF_MEMORY, "allocation of %zu bytes for %s failed", bytes, what);
     return fail_hip(e, "hipMalloc");
   }
+  g_live_allocs.fetch_add(1, std::memory_order_relaxed);
   return FLINT_OK;
 }
 
@@ -373,6 +385,8 @@ int flint_moe_debug_set_epoch(flint_moe_t h, uint32_t epoch) {
   h->epoch = epoch;
   return FLINT_OK;
 }
+
+int flint_moe_debug_live_allocations(void) { return g_live_allocs.load(std::memory_order_relaxed); }
 
 void flint_moe_destroy(flint_moe_t h) { release(h); }
 

@@ -149,29 +149,35 @@ def test_invalid_arguments_rejected(model):
 
 
 CREATE_ALLOCATIONS = 10   # device allocations of one create call
+RUNTIME_CHUNKS = 2 * (2 << 20)   # two of the HIP runtime's 2 MiB small-buffer chunks
 
 
 def test_allocation_failure_is_reported_and_releases_everything(model):
     """Create failing at each of its device allocations in turn: the error is
-    reported, and what the call had allocated until then is freed (device
-    memory returns to exactly its level before the call).  Then a full
-    create / forward / destroy cycle leaves device memory as it found it
-    (measured after one such cycle: the HIP runtime keeps the 2 MiB chunks it
-    carves small buffers from, and the partial creates above change which of
-    those it holds)."""
+    reported, and what the call had allocated until then is freed.  The
+    library's own count of live device allocations is exact; device-level free
+    memory is checked one-sided only, since the HIP runtime may keep freed
+    blocks for reuse and return them to the device later (a block freed by an
+    earlier destroy has come back during a later create), and keeps the 2 MiB
+    chunks it carves small buffers from, so free memory can rise between the
+    steps but must never fall below where it started by more than two such
+    chunks."""
     synth, m, ids, w = model
     layers = build_layers(fg.Synth(FL, seed=1, n_layers=1), [0])
     x = torch.from_numpy(fg.tokens(0, [7])).cuda()
 
     def create_run_close():
         m2 = F.FlintMoE(layers)
+        assert F.flint_moe_debug_live_allocations() == live0 + CREATE_ALLOCATIONS
         out = m2.forward(x, 0, 1)
         torch.cuda.synchronize()
         m2.status()
         m2.close()
         return out
 
+    live0 = F.flint_moe_debug_live_allocations()   # the module's model holds its own
     create_run_close()   # first: the runtime's lazy set-up (e.g. of the first cooperative launch) is done
+    assert F.flint_moe_debug_live_allocations() == live0
     torch.cuda.empty_cache()
     free0 = torch.cuda.mem_get_info()[0]
     try:
@@ -181,18 +187,19 @@ def test_allocation_failure_is_reported_and_releases_everything(model):
                 F.FlintMoE(layers)
             assert ei.value.code == F.FLINT_ERR_OUT_OF_MEMORY
             assert f"allocation {k} " in str(ei.value)
-            assert torch.cuda.mem_get_info()[0] == free0, k
+            assert F.flint_moe_debug_live_allocations() == live0, k
+            assert torch.cuda.mem_get_info()[0] >= free0 - RUNTIME_CHUNKS, k
         os.environ["FLINT_MOE_FAIL_ALLOC"] = str(CREATE_ALLOCATIONS + 1)   # past the last one: no failure
         out = create_run_close()
     finally:
         del os.environ["FLINT_MOE_FAIL_ALLOC"]
     assert torch.isfinite(out).all()
+    assert F.flint_moe_debug_live_allocations() == live0
     del out
     torch.cuda.empty_cache()            # the output tensor was torch's, not the library's
-    free1 = torch.cuda.mem_get_info()[0]
-    create_run_close()
-    torch.cuda.empty_cache()
-    assert torch.cuda.mem_get_info()[0] == free1
+    # the runtime carves the small buffers (error word, layer table) from 2 MiB
+    # chunks that it keeps once made; the exact check is the count above
+    assert torch.cuda.mem_get_info()[0] >= free0 - RUNTIME_CHUNKS
 
 
 def test_persistent_and_layered_modes_agree_bitwise(model):
