@@ -118,8 +118,10 @@ __global__ void __launch_bounds__(PF_NT) k_pf_input(const float* __restrict__ x,
 // 32 tokens x 32 experts per workgroup.  Wave w sums K in [512 w, 512 w + 512)
 // with two interleaved accumulators (short dependency chains), and the four
 // partial sums are added in wave order.
-__global__ void __launch_bounds__(PF_NT) k_pf_router(const uint16_t* __restrict__ a, int n,
-                                                      const uint16_t* __restrict__ router, float* __restrict__ z) {
+// (a and router are not marked __restrict__: the compiler fence below must
+// order their loads, which it does not for memory known to be read-only)
+__global__ void __launch_bounds__(PF_NT) k_pf_router(const uint16_t* a, int n, const uint16_t* router,
+                                                      float* __restrict__ z) {
   __shared__ float part[3][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lrow = lane & 31, hl = lane >> 5;
   const int m0 = blockIdx.x * 32, e = blockIdx.y * 32 + lrow;
@@ -127,10 +129,37 @@ __global__ void __launch_bounds__(PF_NT) k_pf_router(const uint16_t* __restrict_
   const uint4* ar = reinterpret_cast<const uint4*>(a + (size_t)m * H) + wave * 64 + hl;
   const uint4* wr = reinterpret_cast<const uint4*>(router + (size_t)e * H) + wave * 64 + hl;
   pf_f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 4
-  for (int j = 0; j < 32; j += 2) {   // MFMA step j: chunks 2 j (lanes 0..31) and 2 j + 1 (lanes 32..63)
-    acc0 = mfma_bf16(ar[2 * j], to_pair_order(wr[2 * j]), acc0);
-    acc1 = mfma_bf16(ar[2 * j + 2], to_pair_order(wr[2 * j + 2]), acc1);
+  // MFMA step j: chunks 2 j (lanes 0..31) and 2 j + 1 (lanes 32..63).  The
+  // operands of eight steps are requested as one batch, the next batch before
+  // the current one is used (left to itself the compiler interleaves each
+  // load with its use, about four in flight per wave).
+  constexpr int RB = 8;
+  uint4 av[2][RB], wv[2][RB];
+  auto load = [&](int buf, int j0) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      av[buf][i] = ar[2 * (j0 + i)];
+      wv[buf][i] = wr[2 * (j0 + i)];
+    }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int b = 0; b < 32 / RB; ++b) {
+    if (b + 1 < 32 / RB) load((b + 1) & 1, RB * (b + 1));
+    compiler_fence();
+    // the current batch's operands pass through an empty asm statement after
+    // the fence, so its MFMAs cannot be hoisted above the next batch's loads
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      uint4& x = av[b & 1][i];
+      uint4& y = wv[b & 1][i];
+      asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w), "+v"(y.x), "+v"(y.y), "+v"(y.z), "+v"(y.w));
+    }
+#pragma unroll
+    for (int i = 0; i < RB; i += 2) {
+      acc0 = mfma_bf16(av[b & 1][i], to_pair_order(wv[b & 1][i]), acc0);
+      acc1 = mfma_bf16(av[b & 1][i + 1], to_pair_order(wv[b & 1][i + 1]), acc1);
+    }
   }
   if (wave > 0) {
 #pragma unroll
