@@ -708,19 +708,31 @@ __global__ void __launch_bounds__(PR_NT) k_pf_sh_down(const float* xin, float* o
     pr_prologue<IS, 1, PR_D>(W, S, wrow0, ring);
     pr_stage_store<IS, 2>(T, v);
     wg_sync();
+    // the epilogue's routed outputs and residual, requested after the tile's
+    // stores (a wait for those would otherwise cover these loads too: the
+    // memory counter retires in order) so that they arrive during the K loop;
+    // rows past n repeat the last token and are not used
+    const int col = wrow0 + lrow;
+    float yv[16][TOPK], xv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = min(m0 + pr_row(r), n - 1);
+      const float* yt = y + (size_t)t * TOPK * H + col;
+#pragma unroll
+      for (int s = 0; s < TOPK; ++s) yv[r][s] = yt[(size_t)s * H];
+      xv[r] = xin[(size_t)t * H + col];
+    }
     pr_compute<IS, 2, 1, 1, PR_D>(T, W, S, wrow0, ring, [&](int nb, const pf_f32x16 (&acc)[1]) {
-      const int col = wrow0 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = m0 + pr_row(r);
         if (t < n) {
           const float* wt = w + (size_t)t * TOPK;
-          const float* yt = y + (size_t)t * TOPK * H + col;
-          float d = wt[0] * yt[0];
+          float d = wt[0] * yv[r][0];
 #pragma unroll
-          for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yt[(size_t)s * H], d);
+          for (int s = 1; s < TOPK; ++s) d = fmaf(wt[s], yv[r][s], d);
           d += acc[0][r];
-          out[(size_t)t * H + col] = xin[(size_t)t * H + col] + d;
+          out[(size_t)t * H + col] = xv[r] + d;
         }
       }
     });
