@@ -137,9 +137,9 @@ __device__ __forceinline__ bool has_empty(uint4 v) {
 }
 
 // Wait until values src[0..nvals) (nvals a multiple of 4) are all written;
-// hand value j to sink(j, value).  Thread i polls the 16-byte groups
-// i + NTHR k, k < K.  Returns false on timeout (the device error word is then
-// set).
+// hand values j .. j + 3 (j a multiple of 4) to sink(j, values).  Thread i
+// polls the 16-byte groups i + NTHR k, k < K.  Returns false on timeout (the
+// device error word is then set).
 template <int K, typename Sink, int NTHR = NT>
 __device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, int* err, Sink sink, int tid,
                                               int dbg_layer, int dbg_id, GtsLds gts_lds) {
@@ -179,12 +179,7 @@ __device__ __forceinline__ bool gather_values(const uint32_t* src, int nvals, in
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int j = tid + NTHR * k;
-    if (j < ngroups) {
-      sink(4 * j, v[k].x);
-      sink(4 * j + 1, v[k].y);
-      sink(4 * j + 2, v[k].z);
-      sink(4 * j + 3, v[k].w);
-    }
+    if (j < ngroups) sink(4 * j, v[k]);
   }
   return true;
 }
@@ -221,20 +216,27 @@ struct HPosWG {
   }
 };
 
-// Where the single-token gathers put their values in LDS.
-struct StoreAt {   // value j -> dst[j]
+// Where the single-token gathers put their values in LDS: four values at a
+// time, values j .. j + 3 of a 16-byte group (j a multiple of 4).  The layouts
+// map each such group to four consecutive, 16-byte aligned LDS words (for h:
+// a workgroup's run of 16 values splits into groups of one kind, shared or
+// routed, each 4-aligned, and the transposed position keeps the low two bits
+// of the index), so one address and one 16-byte store serve the group.
+struct StoreAt {   // values j.. -> dst[j..]
   uint32_t* dst;
-  __device__ void operator()(int j, uint32_t v) const { dst[j] = v; }
+  __device__ void operator()(int j, uint4 v) const { *reinterpret_cast<uint4*>(dst + j) = v; }
 };
-struct StoreH {    // fp32 h word j (workgroup-major) -> its transposed position
+struct StoreH {    // fp32 h words j.. (workgroup-major) -> their transposed positions
   uint32_t* dst;
-  __device__ void operator()(int j, uint32_t v) const { dst[HPosWG()(j)] = v; }
+  __device__ void operator()(int j, uint4 v) const { *reinterpret_cast<uint4*>(dst + HPosWG()(j)) = v; }
 };
-struct StoreH16 {  // word j = fp16 h values 2 j (low half) and 2 j + 1 -> fp32 at their positions
+struct StoreH16 {  // words j.. = fp16 h values 2 j .. 2 j + 7 (low half first) -> fp32 at their positions
   float* dst;
-  __device__ void operator()(int j, uint32_t v) const {
-    dst[HPosWG()(2 * j)] = __half2float(__ushort_as_half((unsigned short)(v & 0xFFFFu)));
-    dst[HPosWG()(2 * j + 1)] = __half2float(__ushort_as_half((unsigned short)(v >> 16)));
+  __device__ static float lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xFFFFu))); }
+  __device__ static float hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
+  __device__ void operator()(int j, uint4 v) const {
+    *reinterpret_cast<float4*>(dst + HPosWG()(2 * j)) = make_float4(lo(v.x), hi(v.x), lo(v.y), hi(v.y));
+    *reinterpret_cast<float4*>(dst + HPosWG()(2 * j + 4)) = make_float4(lo(v.z), hi(v.z), lo(v.w), hi(v.w));
   }
 };
 
