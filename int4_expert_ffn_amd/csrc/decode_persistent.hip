@@ -778,11 +778,13 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
     if (sync_or(!ok)) return;
     {
       const int sub = lane & 15;
-      auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
-      auto load_b = [&] {
-        return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
-                           : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
-      };
+      // this token's h chunks are the same for every output row of the wave:
+      // read and summed once, before the rows
+      const HChunk hca = load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32);
+      const HChunk hcb = (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
+                                     : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
+      auto load_a = [&] { return hca; };
+      auto load_b = [&] { return hcb; };
       float wsc[TOPK];   // fp16 form: routed weights times the pack's divisor
 #pragma unroll
       for (int i = 0; i < TOPK; ++i) wsc[i] = F16H ? w_l[i] * A.interm_mult : 0.f;
@@ -1014,11 +1016,13 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
     if (sync_or(!ok)) return;
     {
       const int sub = lane & 15;
-      auto load_a = [&] { return load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32); };
-      auto load_b = [&] {
-        return (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
-                           : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
-      };
+      // this token's h chunks are the same for every output row of the wave:
+      // read and summed once, before the rows
+      const HChunk hca = load_chunk_transposed(hbuf + (lane >> 4) * I, sub, I / 32);
+      const HChunk hcb = (lane < 32) ? load_chunk_transposed(hbuf + (4 + (lane >> 4)) * I, sub, I / 32)
+                                     : load_chunk_transposed(hbuf + TOPK * I, lane - 32, IS / 32);
+      auto load_a = [&] { return hca; };
+      auto load_b = [&] { return hcb; };
       // unrolled with a fixed bound: the prefetched codes are renamed, never
       // copied (a copy would wait for the load in flight)
       float wsc[TOPK];   // fp16 form: routed weights times the pack's divisor
