@@ -417,11 +417,12 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     const int* dl = (n == 1) ? ids_l[0] : list;
     PHASE_MARK(7);
     // down codes of the first token for output row 8 w + wave: needed after the
-    // h exchange; loaded now so that nothing slow is in flight while polling
+    // h exchange.  Requested right behind this wave's first gate/up batch, so
+    // that the memory returns the gate/up rows first and the down rows stream
+    // in while gate/up is computed; they arrive before the h exchange's polls.
     const int row = NWAVES * w + wave;
     uint4 ca0, cb0;
     uint32_t sa0, sb0;
-    load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
     {
       // Row-pair tasks of this workgroup: 4 shared-expert rows (4 w .. 4 w + 3,
       // weights prefetched) and R = 2 D routed rows (w R .. w R + R - 1 of the
@@ -470,6 +471,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       };
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
+      load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
       if (wave == PUB_WAVE) {   // routing weights, while this wave's loads fly (needed after the h exchange)
         int sel[TOPK];
 #pragma unroll
@@ -692,11 +694,12 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       A.trace_ids[o] = ids_l[lane];
       A.trace_w[o] = w_l[lane];
     }
-    // down codes of this wave's first output row: needed after the h exchange
+    // down codes of this wave's first output row: needed after the h exchange,
+    // requested right behind the first gate/up batch so that those rows return
+    // first
     const int row0 = NOUT * u + wave;
     uint4 ca0, cb0;
     uint32_t sa0, sb0;
-    load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
     {
       // task j: j < NSH shared row NSH u + j, else routed row q = NRT u + j - NSH
       // of the token's experts in pick order (slot q / I, row q % I); task j
@@ -751,6 +754,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       static_assert((NTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
       Batch ba, bb;
       load_batch(wave, ba);
+      load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
 #pragma unroll
       for (int k = 0; k < NTASK / NWAVES / (2 * TB); ++k) {
         const int j0 = wave + k * 2 * TB * NWAVES;
