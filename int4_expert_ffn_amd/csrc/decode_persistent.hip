@@ -22,6 +22,7 @@
 // so both launch modes give bitwise-identical results.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -831,7 +832,9 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
 // size does not grow with n.  Every row is computed by the same device
 // function with the same reduction shape as in a single-token call, so each
 // token's result is bitwise the same as running it alone.  F16H as above.
-template <int K, bool F16H>
+// NPAIR: pairs of gate/up batches every workgroup runs (enough for the
+// workgroup of the call with the most tasks; chosen on the host from n).
+template <int K, bool F16H, int NPAIR>
 __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
   constexpr int MSH = 4 * K, MRT = 12 * K, MTASK = MSH + MRT;   // most gate/up row pairs of a workgroup
   constexpr int MOUT = 8 * K;                                   // most output rows of a workgroup
@@ -955,9 +958,10 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
       // the token's experts in pick order (slot q / I, row q % I); task j goes
       // to wave j % 8.  Batches of TB tasks in two register sets: the next
       // batch's rows are requested before the current one is computed.  The
-      // loop runs the most batches any workgroup has (a fixed count), its loads
-      // unconditional (tasks past the last re-read it), so each wait counts
-      // exactly the loads issued after the ones it needs.
+      // loop runs the most batches any workgroup of the call has (a count
+      // fixed at compile time), its loads unconditional (tasks past the last
+      // re-read it), so each wait counts exactly the loads issued after the
+      // ones it needs.
       constexpr int TB = 2;
       struct Batch {
         uint4 qg[TB], qu[TB];
@@ -991,10 +995,11 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
         }
       };
       static_assert((MTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
+      static_assert(NPAIR >= 1 && NPAIR <= MTASK / NWAVES / (2 * TB), "batch pairs");
       Batch ba, bb;
       load_batch(wave, ba);
 #pragma unroll
-      for (int k = 0; k < MTASK / NWAVES / (2 * TB); ++k) {
+      for (int k = 0; k < NPAIR; ++k) {
         const int j0 = wave + k * 2 * TB * NWAVES;
         load_batch(j0 + TB * NWAVES, bb);
         compute_batch(j0, ba);
@@ -1065,18 +1070,39 @@ __global__ void k_clear_words(uint64_t* p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// Pairs of gate/up batches the exact-range kernel needs for n tokens: the
+// most shared + routed row pairs of any workgroup (the same ranges as the
+// kernel's), 2 TB NWAVES = 32 tasks per pair.
+static int exact_batch_pairs(int n) {
+  const int P = NWG / n;
+  int most = 0;
+  for (int u = 0; u < P; ++u) {
+    auto cnt = [&](int T) { return T * (u + 1) / P - T * u / P; };
+    most = std::max(most, cnt(IS) + cnt(TOPK * I));
+  }
+  return (most + 31) / 32;
+}
+
 // The kernel for K-token groups (K = 1: the one-token schedule); F16H: the
-// fp16-intermediate form.
+// fp16-intermediate form.  The exact-range kernels come with the batch-pair
+// counts that 5..15 tokens need, rounded up to one that is built.
 template <bool F16H>
-static const void* decode_kernel(int K, bool exact) {
+static const void* decode_kernel(int K, bool exact, int n) {
   if (K == 2) return reinterpret_cast<const void*>(k_decode_groups<2, F16H>);
   if (K == 4) return reinterpret_cast<const void*>(k_decode_groups<4, F16H>);   // 3, 4 tokens: never exact
-  if (K == 8)
-    return exact ? reinterpret_cast<const void*>(k_decode_groups_any<8, F16H>)
-                 : reinterpret_cast<const void*>(k_decode_groups<8, F16H>);
-  if (K == 16)
-    return exact ? reinterpret_cast<const void*>(k_decode_groups_any<16, F16H>)
-                 : reinterpret_cast<const void*>(k_decode_groups<16, F16H>);
+  if (K == 8) {
+    if (!exact) return reinterpret_cast<const void*>(k_decode_groups<8, F16H>);
+    return exact_batch_pairs(n) <= 3 ? reinterpret_cast<const void*>(k_decode_groups_any<8, F16H, 3>)
+                                     : reinterpret_cast<const void*>(k_decode_groups_any<8, F16H, 4>);
+  }
+  if (K == 16) {
+    if (!exact) return reinterpret_cast<const void*>(k_decode_groups<16, F16H>);
+    const int np = exact_batch_pairs(n);
+    return np <= 5   ? reinterpret_cast<const void*>(k_decode_groups_any<16, F16H, 5>)
+           : np <= 6 ? reinterpret_cast<const void*>(k_decode_groups_any<16, F16H, 6>)
+           : np <= 7 ? reinterpret_cast<const void*>(k_decode_groups_any<16, F16H, 7>)
+                     : reinterpret_cast<const void*>(k_decode_groups_any<16, F16H, 8>);
+  }
   return reinterpret_cast<const void*>(k_decode_persistent<F16H>);
 }
 
@@ -1086,7 +1112,7 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   // One token: the schedule above.  Otherwise groups for K tokens, K the
   // power of two at or above n: the statically sized kernel leaves K - n
   // groups idle, the exact-range kernel uses every workgroup; measured, the
-  // exact ranges win up to n = 0.75 K.
+  // exact ranges win up to n = 13 K / 16 (5, 6 and 9..13 tokens).
   const int n = a.n;
   const int K = n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
   // FLINT_MOE_GROUPS=exact or =pow2 forces one form for every n that is not a
@@ -1095,8 +1121,8 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
     const char* v = getenv("FLINT_MOE_GROUPS");
     return !v ? 0 : strcmp(v, "exact") == 0 ? 1 : strcmp(v, "pow2") == 0 ? 2 : 0;
   }();
-  const bool exact = force == 1 ? n != K : force == 2 ? false : 4 * n <= 3 * K;
-  const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact) : decode_kernel<false>(K, exact);
+  const bool exact = force == 1 ? n != K : force == 2 ? false : 16 * n <= 13 * K;
+  const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact, n) : decode_kernel<false>(K, exact, n);
   return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
 }
 

@@ -147,11 +147,12 @@ def test_fp16_interm_deterministic_and_decode_only(models):
     assert ei.value.code == F.FLINT_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("n", [2, 3, 5, 8, 9, 16])
+@pytest.mark.parametrize("n", [2, 3, 5, 6, 8, 9, 10, 12, 16])
 def test_fp16_interm_token_groups_match_single_tokens(models, n):
     """Several tokens per call (every group kernel: 2, 4 and 8 and 16 tokens
-    per group size, exact ranges for 5 and 9): each token's output over the
-    three layers is bitwise the one-token call's."""
+    per group size, exact ranges for 5, 6, 9, 10 and 12, each with its own
+    batch count): each token's output over the three layers is bitwise the
+    one-token call's."""
     pack, m16, m32, ids, w = models
     x = torch.from_numpy(fg.tokens(2, range(100, 100 + n))).cuda()
     together = m16.forward(x)
