@@ -756,12 +756,13 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       Batch ba, bb;
       load_batch(wave, ba);
       load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
+      constexpr int NPAIR = NTASK / NWAVES / (2 * TB);
 #pragma unroll
-      for (int k = 0; k < NTASK / NWAVES / (2 * TB); ++k) {
+      for (int k = 0; k < NPAIR; ++k) {
         const int j0 = wave + k * 2 * TB * NWAVES;
         load_batch(j0 + TB * NWAVES, bb);
         compute_batch(j0, ba);
-        load_batch(j0 + 2 * TB * NWAVES, ba);   // past the last task: a cached re-read, never used
+        if (k + 1 < NPAIR) load_batch(j0 + 2 * TB * NWAVES, ba);   // known at compile time
         compute_batch(j0 + TB * NWAVES, bb);
       }
     }
@@ -1003,7 +1004,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
         const int j0 = wave + k * 2 * TB * NWAVES;
         load_batch(j0 + TB * NWAVES, bb);
         compute_batch(j0, ba);
-        load_batch(j0 + 2 * TB * NWAVES, ba);   // past the last task: a cached re-read, never used
+        if (k + 1 < NPAIR) load_batch(j0 + 2 * TB * NWAVES, ba);   // known at compile time
         compute_batch(j0 + TB * NWAVES, bb);
       }
     }
