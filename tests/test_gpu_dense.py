@@ -127,17 +127,25 @@ def test_dense_mlp_parity(dense):
 
 
 def test_dense_mlp_batch_invariance_in_place_and_zero(dense):
+    """Every token's h and out are bitwise the same for any token count (1, 2,
+    3, 4, 7 and 16 tokens per call), also in place (out = x)."""
     inter, w, wc = dense
     x = fg.tokens(4, range(16))
     h1, o1 = run_dense(inter, w, x[:1])
+    h4, o4 = run_dense(inter, w, x[:4])
     h7, o7 = run_dense(inter, w, x[:7])
     h16, o16 = run_dense(inter, w, x)
     assert np.array_equal(h16[:1], h1) and np.array_equal(o16[:1], o1)
+    assert np.array_equal(h16[:4], h4) and np.array_equal(o16[:4], o4)
     assert np.array_equal(h16[:7], h7) and np.array_equal(o16[:7], o7)
     hi, oi = run_dense(inter, w, x, out_is_x=True)
     assert np.array_equal(hi, h16) and np.array_equal(oi, o16)
+    hi3, oi3 = run_dense(inter, w, x[:3], out_is_x=True)
+    assert np.array_equal(hi3, h16[:3]) and np.array_equal(oi3, o16[:3])
     hz, oz = run_dense(inter, w, np.zeros((3, H), np.float32))
     assert np.all(hz == 0) and np.all(oz == 0)
+    h2, o2 = run_dense(inter, w, x[4:6])
+    assert np.array_equal(h2, h16[4:6]) and np.array_equal(o2, o16[4:6])
 
 
 def test_dense_mlp_power_of_two_up_scale_is_exact(dense):
