@@ -1,6 +1,6 @@
-// Decode path, persistent form: one cooperative launch runs every layer of a
-// forward call on 256 workgroups (one per CU), with no kernel boundaries
-// between the dependent stages of a layer.
+// Decode path, persistent form: one launch runs every layer of a forward call
+// on 256 resident workgroups (one per CU), with no kernel boundaries between
+// the dependent stages of a layer.
 //
 // Work of workgroup w (8 wavefronts) in layer l, for each token:
 //   P0  block input a = bf16(rmsnorm(x_l)) (every workgroup, redundantly)
@@ -25,6 +25,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "decode_common.h"
 #include "decode_persistent.h"
@@ -1107,6 +1108,48 @@ static const void* decode_kernel(int K, bool exact, int n) {
   return reinterpret_cast<const void*>(k_decode_persistent<F16H>);
 }
 
+// Launch of a persistent kernel: NWG workgroups that must all be resident at
+// once (one per CU: their LDS allows no second one).  They are launched as
+// ordinary kernels.  A cooperative launch would guarantee co-residency, but
+// on this runtime it costs about 20 us per call, against a 590 us kernel.
+// What the guarantee prevents is handled here instead:
+// - Two persistent launches from different streams could each hold part of
+//   the CUs and wait for workgroups that cannot be placed.  So a launch on a
+//   stream other than the previous launch's (of any handle on this device)
+//   first waits for that launch: an event is recorded behind every launch.
+// - Other work on the GPU can only delay the placement of some workgroups.
+//   Every wait in the kernels is bounded (1 s), so a launch that cannot get
+//   its CUs ends with the device error word set instead of hanging.
+// The handle requires a GPU with exactly NWG CUs, and each kernel's LDS and
+// register use (checked at compile time) let one workgroup fit a CU.
+static hipError_t launch_resident(const void* k, void** kargs, hipStream_t s) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static hipEvent_t done[MAX_DEV] = {};
+  static hipStream_t last[MAX_DEV] = {};
+  static bool used[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[dev]) {
+    e = hipEventCreateWithFlags(&done[dev], hipEventDisableTiming);
+    if (e != hipSuccess) { done[dev] = nullptr; return e; }
+  }
+  if (used[dev] && last[dev] != s) {
+    e = hipStreamWaitEvent(s, done[dev], 0);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(done[dev], s);
+  if (e != hipSuccess) return e;
+  last[dev] = s;
+  used[dev] = true;
+  return hipSuccess;
+}
+
 hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   PersistArgs a = args;
   void* kargs[] = {&a};
@@ -1124,7 +1167,7 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
   }();
   const bool exact = force == 1 ? n != K : force == 2 ? false : 16 * n <= 13 * K;
   const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact, n) : decode_kernel<false>(K, exact, n);
-  return hipLaunchCooperativeKernel(k, dim3(NWG), dim3(NT), kargs, 0, s);
+  return launch_resident(k, kargs, s);
 }
 
 hipError_t clear_exchange(uint64_t* p, size_t n_words, hipStream_t s) {

@@ -249,7 +249,8 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
   if (rc) { release(h); return rc; }
   e = hipMemset(h->dev_error, 0, 256);
   if (e != hipSuccess) { rc = fail_hip(e, "create"); release(h); return rc; }
-  // persistent decode: needs cooperative launch on exactly NWG compute units
+  // persistent decode: needs exactly NWG compute units, all resident at once
+  // (the device must support the co-resident launch model)
   {
     int cus = 0, coop = 0;
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device);

@@ -300,3 +300,34 @@ def test_exchange_tag_wrap_clears_buffers_and_keeps_results(model):
     m.status()
     for i, (o, kind) in enumerate(outs):
         assert torch.equal(o, ref4 if kind else ref1), i
+
+
+def test_persistent_launches_from_two_streams(model):
+    """Two handles on two streams, calls queued alternately with no host
+    synchronisation: the persistent kernels need every workgroup resident at
+    once, so a launch on another stream than the previous one waits for it.
+    Each handle's results must equal the same calls run on one stream."""
+    synth, m, ids, w = model
+    layers = build_layers(synth, range(N_LAYERS))
+    m2 = F.FlintMoE(layers)
+    del layers
+    x = torch.from_numpy(fg.tokens(0, range(800, 816))).cuda()
+    calls = [(1, 0, N_LAYERS), (3, 0, 2), (1, 1, N_LAYERS), (9, 0, N_LAYERS), (1, 0, N_LAYERS), (16, 0, N_LAYERS)]
+    try:
+        torch.cuda.synchronize()
+        refs = [m.forward(x[:n].contiguous(), l0, l1) for n, l0, l1 in calls]
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = []
+        for i, (n, l0, l1) in enumerate(calls):
+            for hm, st in ((m, s1), (m2, s2)):
+                with torch.cuda.stream(st):
+                    outs.append(hm.forward(x[:n].contiguous(), l0, l1, stream=st.cuda_stream))
+        torch.cuda.synchronize()
+        m.status()
+        m2.status()
+        for i in range(len(calls)):
+            assert torch.equal(outs[2 * i], refs[i]), ("stream 1", i, calls[i])
+            assert torch.equal(outs[2 * i + 1], refs[i]), ("stream 2", i, calls[i])
+    finally:
+        m2.close()
