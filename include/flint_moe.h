@@ -118,7 +118,9 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
  * is allowed; partial overlap is not.  1 <= n_tokens <= FLINT_MAX_TOKENS and
  * 0 <= layer_begin < layer_end <= n_layers.  Asynchronous on `stream` (a
  * hipStream_t; NULL = the default stream).  One handle serves one stream at a
- * time: calls on a handle must not overlap.  A call must not be captured into
+ * time: calls on a handle must not overlap.  Decode calls (n_tokens <= 16)
+ * need the whole GPU at once: a decode call on another stream than the
+ * previous decode call on the device (of any handle) waits for that call.  A call must not be captured into
  * a HIP graph for replay: each call takes per-call state from the host (the
  * tags and slot parity of its exchanges between workgroups).  For n_tokens <= 16 each token's
  * result is bitwise independent of n_tokens (decode path).  Larger calls take
