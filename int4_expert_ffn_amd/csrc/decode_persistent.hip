@@ -419,9 +419,9 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
     const int* dl = (n == 1) ? ids_l[0] : list;
     PHASE_MARK(7);
     // down codes of the first token for output row 8 w + wave: needed after the
-    // h exchange.  Requested right behind this wave's first gate/up batch, so
-    // that the memory returns the gate/up rows first and the down rows stream
-    // in while gate/up is computed; they arrive before the h exchange's polls.
+    // h exchange.  Requested once this wave's gate/up rows are computed, so
+    // that the gate/up rows do not share the memory's bandwidth with them;
+    // they arrive during the h exchange (whose first poll waits for them).
     const int row = NWAVES * w + wave;
     uint4 ca0, cb0;
     uint32_t sa0, sb0;
@@ -473,7 +473,6 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
       };
       int j0 = 4 + ((wave - 4 + NWAVES) % NWAVES);   // first routed task of this wave
       load_batch(j0);
-      load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
       if (wave == PUB_WAVE) {   // routing weights, while this wave's loads fly (needed after the h exchange)
         int sel[TOPK];
 #pragma unroll
@@ -496,6 +495,7 @@ __global__ void __launch_bounds__(NT) k_decode_persistent(PersistArgs A) {
         load_batch(j0);
         compute_batch(j0);
       }
+      load_down_row(L, ids_l[0], row, ca0, sa0, cb0, sb0);
     }
     wg_sync();
     PUB_MARK(13);
@@ -697,8 +697,8 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       A.trace_w[o] = w_l[lane];
     }
     // down codes of this wave's first output row: needed after the h exchange,
-    // requested right behind the first gate/up batch so that those rows return
-    // first
+    // requested after the gate/up rows (they then do not share the memory's
+    // bandwidth with them)
     const int row0 = NOUT * u + wave;
     uint4 ca0, cb0;
     uint32_t sa0, sb0;
@@ -756,7 +756,6 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       static_assert((NTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
       Batch ba, bb;
       load_batch(wave, ba);
-      load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
       constexpr int NPAIR = NTASK / NWAVES / (2 * TB);
 #pragma unroll
       for (int k = 0; k < NPAIR; ++k) {
@@ -766,6 +765,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
         if (k + 1 < NPAIR) load_batch(j0 + 2 * TB * NWAVES, ba);   // known at compile time
         compute_batch(j0 + TB * NWAVES, bb);
       }
+      load_down_row(L, ids_l, row0, ca0, sa0, cb0, sb0);
     }
     wg_sync();
     if (wave == PUB_WAVE) {
