@@ -680,6 +680,27 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
         publish(A.xz + (size_t)t * 4 * E + 4 * K * u + lane, tag, pw == 0 ? c_lo : pw == 1 ? c_hi : pw == 2 ? s_lo : s_hi);
     }
 
+    // gate/up row pairs come in batches of TB tasks (below).  With K >= 4 the
+    // first batch holds shared rows only, which do not depend on the routing:
+    // it is requested before the (c, s) exchange, whose wait hides it.
+    constexpr int TB = 2;
+    struct Batch {
+      uint4 qg[TB], qu[TB];
+      uint32_t qsg[TB], qsu[TB];
+    };
+    constexpr bool EARLY = NSH >= TB * NWAVES;
+    Batch ba;
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        const size_t rr = (size_t)NSH * u + wave + b * NWAVES;
+        ba.qg[b] = reinterpret_cast<const uint4*>(L.sh_gate + rr * (H / 2))[lane];
+        ba.qu[b] = reinterpret_cast<const uint4*>(L.sh_up + rr * (H / 2))[lane];
+        ba.qsg[b] = L.sh_gate_s[rr * (H / G) + (lane >> 2)];
+        ba.qsu[b] = L.sh_up_s[rr * (H / G) + (lane >> 2)];
+      }
+    }
+
     // ---------------- P2: routing, gate/up
     ok = true;
     if (poller)
@@ -709,11 +730,6 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       // next batch's rows are requested before the current one is computed.
       // Loads are unconditional (tasks past the last re-read it), so each
       // wait counts exactly the loads issued after the ones it needs.
-      constexpr int TB = 2;
-      struct Batch {
-        uint4 qg[TB], qu[TB];
-        uint32_t qsg[TB], qsu[TB];
-      };
       auto task_row = [&](int j, const uint8_t*& g, const uint16_t*& gs, const uint8_t*& up, const uint16_t*& us,
                           size_t& rr) {
         if (j < NSH) {
@@ -754,8 +770,8 @@ __global__ void __launch_bounds__(NT) k_decode_groups(PersistArgs A) {
       };
       // NTASK / 8 = 2 K tasks per wave: an even number of batches of 2
       static_assert((NTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
-      Batch ba, bb;
-      load_batch(wave, ba);
+      Batch bb;
+      if constexpr (!EARLY) load_batch(wave, ba);
       constexpr int NPAIR = NTASK / NWAVES / (2 * TB);
 #pragma unroll
       for (int k = 0; k < NPAIR; ++k) {
