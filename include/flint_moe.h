@@ -120,9 +120,12 @@ int flint_moe_create_fp16_interm(const flint_moe_layer* weights, int n_layers, i
  * hipStream_t; NULL = the default stream).  One handle serves one stream at a
  * time: calls on a handle must not overlap.  Decode calls (n_tokens <= 16)
  * need the whole GPU at once: a decode call on another stream than the
- * previous decode call on the device (of any handle) waits for that call.  A call must not be captured into
- * a HIP graph for replay: each call takes per-call state from the host (the
- * tags and slot parity of its exchanges between workgroups).  For n_tokens <= 16 each token's
+ * previous decode call on the device (of any handle in this process) waits
+ * for that call.  If other work keeps part of the GPU busy for more than a
+ * second, the call stops and flint_moe_status reports FLINT_ERR_DEVICE.
+ * A call must not be captured into a HIP graph for replay: each call takes
+ * per-call state from the host (the tags and slot parity of its exchanges
+ * between workgroups).  For n_tokens <= 16 each token's
  * result is bitwise independent of n_tokens (decode path).  Larger calls take
  * the prefill path: tokens sorted by expert, grouped GEMMs on the matrix
  * cores, the SwiGLU output kept as two bf16 parts (about 16 significant bits)
