@@ -952,6 +952,25 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
     }
 
     // ---------------- P2: routing, gate/up
+    // gate/up row pairs come in batches of TB tasks (below).  The first batch
+    // (tasks wave and wave + 8) holds shared rows only, which do not depend on
+    // the routing (every workgroup of these calls has nsh >= 20 shared row
+    // pairs: at most 51 workgroups per token): it is requested before the
+    // (c, s) exchange, whose wait hides it.
+    constexpr int TB = 2;
+    struct Batch {
+      uint4 qg[TB], qu[TB];
+      uint32_t qsg[TB], qsu[TB];
+    };
+    Batch ba;
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      const size_t rr = (size_t)(s0 + min(wave + b * NWAVES, nsh - 1));
+      ba.qg[b] = reinterpret_cast<const uint4*>(L.sh_gate + rr * (H / 2))[lane];
+      ba.qu[b] = reinterpret_cast<const uint4*>(L.sh_up + rr * (H / 2))[lane];
+      ba.qsg[b] = L.sh_gate_s[rr * (H / G) + (lane >> 2)];
+      ba.qsu[b] = L.sh_up_s[rr * (H / G) + (lane >> 2)];
+    }
     ok = true;
     if (poller)
       ok = gather<(4 * E + NPOLL - 1) / NPOLL, ZPos, NPOLL>(A.xz + (size_t)t * 4 * E, 4 * E, tag, stage, A.err,
@@ -980,11 +999,6 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
       // fixed at compile time), its loads unconditional (tasks past the last
       // re-read it), so each wait counts exactly the loads issued after the
       // ones it needs.
-      constexpr int TB = 2;
-      struct Batch {
-        uint4 qg[TB], qu[TB];
-        uint32_t qsg[TB], qsu[TB];
-      };
       auto load_batch = [&](int j0, Batch& bt) {
 #pragma unroll
         for (int b = 0; b < TB; ++b) {
@@ -1014,8 +1028,7 @@ __global__ void __launch_bounds__(NT) k_decode_groups_any(PersistArgs A) {
       };
       static_assert((MTASK / NWAVES) % (2 * TB) == 0, "batches come in pairs");
       static_assert(NPAIR >= 1 && NPAIR <= MTASK / NWAVES / (2 * TB), "batch pairs");
-      Batch ba, bb;
-      load_batch(wave, ba);
+      Batch bb;
 #pragma unroll
       for (int k = 0; k < NPAIR; ++k) {
         const int j0 = wave + k * 2 * TB * NWAVES;
@@ -1181,7 +1194,8 @@ hipError_t launch_decode_persistent(const PersistArgs& args, hipStream_t s) {
     const char* v = getenv("FLINT_MOE_GROUPS");
     return !v ? 0 : strcmp(v, "exact") == 0 ? 1 : strcmp(v, "pow2") == 0 ? 2 : 0;
   }();
-  const bool exact = force == 1 ? n != K : force == 2 ? false : 16 * n <= 13 * K;
+  // (exact ranges need n >= 5: their first gate/up batch is shared rows only)
+  const bool exact = n >= 5 && (force == 1 ? n != K : force == 2 ? false : 16 * n <= 13 * K);
   const void* k = a.interm_mult != 0.f ? decode_kernel<true>(K, exact, n) : decode_kernel<false>(K, exact, n);
   return launch_resident(k, kargs, s);
 }
