@@ -719,6 +719,36 @@ PHASES = (("x gather", 0, 1), ("norm (block input)", 1, 2), ("router (and the sh
           ("h gather", 8, 9), ("down and combine", 9, 10))
 
 
+def bench_exchange_probe(args):
+    """XCD placement of a 256-workgroup launch and the round trip of one value
+    between two workgroups with the exchanges' store and load policies
+    (profiling build libflint_moe_phase.so, flint_moe_debug_exchange_probe)."""
+    import int4_expert_ffn_amd as F
+    F.LIB_PATH = os.path.join(F.HERE, "libflint_moe_phase.so")
+    if not os.path.exists(F.LIB_PATH):
+        raise FileNotFoundError(f"{F.LIB_PATH} is missing: python -m int4_expert_ffn_amd.build --phase-ts")
+    L = F.lib()
+    L.flint_moe_debug_exchange_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    L.flint_moe_debug_exchange_probe.restype = ctypes.c_int
+    xcc = np.zeros(256, dtype=np.int32)
+    rt = np.zeros(3, dtype=np.float64)
+    rc = L.flint_moe_debug_exchange_probe(xcc.ctypes.data, rt.ctypes.data)
+    assert rc == 0, rc
+    round_robin = int(np.sum(xcc == np.arange(256) % 8))
+    lines = ["# exchange probe: XCD of each workgroup of a 256-workgroup launch (XCC_ID register) and the round trip",
+             "# of one 32-bit value between workgroup 0 and another (stored by one, polled by the other, back), 2,000 rounds",
+             "# command: python -m int4_expert_ffn_amd.build --phase-ts && python bench.py --exchange-probe",
+             f"workgroups on XCD w % 8: {round_robin} of 256",
+             f"xcd of workgroups 0..15: {' '.join(str(int(v)) for v in xcc[:16])}",
+             f"round trip, agent-scope store / sc1 poll, same XCD: {rt[0]:.3f} us",
+             f"round trip, agent-scope store / sc1 poll, other XCD: {rt[1]:.3f} us",
+             f"round trip, sc0 store / sc1 poll, same XCD: {rt[2]:.3f} us"]
+    print("\n".join(lines))
+    if args.exchange_probe_out:
+        with open(args.exchange_probe_out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+
 def bench_phase_table(args):
     """Phase durations of the single-token decode kernel (profiling build
     libflint_moe_phase.so): median over workgroups and over layers 1..46 of
@@ -807,6 +837,9 @@ def _main():
                     help="with --attn: only the batch-1 full layer (for a kernel trace of that one shape)")
     ap.add_argument("--cost-table-tokens", default=None,
                     help="comma-separated token counts for --cost-table (default 1..16)")
+    ap.add_argument("--exchange-probe", action="store_true",
+                    help="XCD placement and workgroup-to-workgroup round trips (profiling build)")
+    ap.add_argument("--exchange-probe-out", default=None, help="write the probe's summary to this file")
     ap.add_argument("--phase-table", action="store_true",
                     help="decode phase timestamps (needs the --phase-ts build of the library)")
     ap.add_argument("--phase-table-out", default=None, help="write the phase table to this file")
@@ -818,6 +851,8 @@ def _main():
     if args.counters_summary:
         summarize_counters(*args.counters_summary, commands=args.command, which=args.counters_kernel)
         return
+    if args.exchange_probe:
+        return bench_exchange_probe(args)
     if args.phase_table:
         return bench_phase_table(args)
     if args.prefill:
